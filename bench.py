@@ -1,0 +1,222 @@
+"""Benchmark: ragged MLA prefill on one MI355X.
+
+Headline: the DeepSeek-V3-shaped ragged batch (16 sequences, lengths drawn
+uniformly in [256, 4096], 128 heads, bf16 Q/K dim 192, V dim 128, causal,
+seed 2). One step = one pass of the hot path over that batch:
+  plan the work list on the host from the indptrs, upload it (async copy on
+  the stream), run the prefill kernel (O and LSE).
+Inputs are resident in HBM before the timed region. The step is timed with
+a barrier + torch.cuda.synchronize() on both sides; the kernel alone is
+timed with HIP events recorded on the stream it is launched on.
+
+FLOPs = 2 * heads * (visible query-key pairs) * (192 + 128) (algorithmic:
+masked work inside partial tiles is not counted).
+
+Also measured in the same run (reported under "secondary"): merge_state at
+the chunked-prefill size (16384 tokens x 128 heads, bf16), against the HBM
+roofline.
+
+cpu_baseline: the fp64 oracle (test infrastructure, timed as it stands) on a
+bounded sample of the same workload's (row, head) pairs, on this host's cores.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import random
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (published: 2.5 PFLOP/s dense)
+PEAK_HBM_GBS = 8000.0         # HBM3E, 8 TB/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs(qo, kv, causal):
+    n = 0
+    for b in range(len(qo) - 1):
+        ql, kl = qo[b + 1] - qo[b], kv[b + 1] - kv[b]
+        if not causal:
+            n += ql * kl
+            continue
+        for_rows = 0
+        # rows i see min(kl, max(0, kl - ql + i + 1)) keys
+        for i in range(ql):
+            for_rows += min(kl, max(0, kl - ql + i + 1))
+        n += for_rows
+    return n
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle baseline sample (0 = skip)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--n-xcd", type=int, default=8)
+    return ap.parse_args()
+
+
+def time_prefill(mra, torch, x, steps, warmup, n_xcd):
+    plan = mra.Plan(n_xcd=n_xcd)
+    out = torch.empty((x.q.shape[0], x.num_heads, 128), dtype=x.q.dtype, device=x.q.device)
+    lse = torch.empty((x.q.shape[0], x.num_heads), dtype=torch.float32, device=x.q.device)
+
+    def step(ev=None):
+        plan.plan(x.qo_indptr, x.kv_indptr, x.num_heads, x.causal, x.q.dtype)
+        plan.upload()
+        if ev is not None:
+            ev[0].record()
+        plan.run(x.q, x.k, x.v, x.sm_scale, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    info = plan.info()
+    return wall, kern_ms, info
+
+
+def cpu_baseline(oracle, torch, x, target_s, seed=0):
+    """Oracle TFLOP/s on a random sample of (row, head) pairs of the workload."""
+    rng = random.Random(seed)
+    qo, kv = x.qo_indptr, x.kv_indptr
+    heads = sorted(rng.sample(range(x.num_heads), min(2, x.num_heads)))
+    host = {h: (x.q[:, h:h + 1].contiguous().cpu(), x.k[:, h:h + 1].contiguous().cpu(),
+                x.v[:, h:h + 1].contiguous().cpu()) for h in heads}
+
+    def keys_seen(t):
+        b = max(i for i in range(len(qo) - 1) if qo[i] <= t)
+        ql, kl = qo[b + 1] - qo[b], kv[b + 1] - kv[b]
+        i = t - qo[b]
+        return kl if not x.causal else min(kl, max(0, kl - ql + i + 1))
+
+    def run(n_rows):
+        rows = sorted(rng.randrange(qo[-1]) for _ in range(n_rows))
+        pairs = sum(keys_seen(t) for t in rows) * len(heads)
+        t0 = time.perf_counter()
+        for h in heads:
+            q, k, v = host[h]
+            oracle.prefill(q, k, v, qo, kv, x.causal, x.sm_scale, rows)
+        return time.perf_counter() - t0, pairs, n_rows
+
+    dt, pairs, n = run(64)
+    n2 = max(64, min(200000, int(64 * target_s / max(dt, 1e-3))))
+    dt, pairs, n = run(n2)
+    flops = 2.0 * pairs * 320
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} random query rows x {len(heads)} heads (heads {heads}) of the same "
+                      f"batch, {pairs} visible pairs, {dt:.1f} s, fp64"}
+
+
+def time_merge(mra, torch, workloads, steps, warmup):
+    tokens, heads = 16384, 128
+    o_a, l_a, o_b, l_b = workloads.merge_inputs(tokens, heads, torch.bfloat16, seed=43,
+                                                device="cuda")
+    out = torch.empty_like(o_a)
+    out_l = torch.empty_like(l_a)
+    for _ in range(warmup):
+        mra.merge_state(o_a, l_a, o_b, l_b, out=out, out_lse=out_l)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        mra.merge_state(o_a, l_a, o_b, l_b, out=out, out_lse=out_l)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    rows = tokens * heads
+    bytes_ = rows * (3 * 128 * 2 + 3 * 4)      # read o_a, o_b, lse_a, lse_b; write o, lse
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"workload": f"merge_state {tokens} tokens x {heads} heads, bf16",
+            "kernel_ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mla_ragged_chunked_amd as mra
+    import workloads
+
+    mra.lib()
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    x = workloads.deepseek_v3_batch(device="cuda")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s: T={x.qo_indptr[-1]} H={x.num_heads}")
+    pairs = visible_pairs(x.qo_indptr, x.kv_indptr, x.causal)
+    flops = 2.0 * x.num_heads * pairs * (192 + 128)
+
+    wall, kern_ms, info = time_prefill(mra, torch, x, args.steps, args.warmup, args.n_xcd)
+    ms_step = wall / args.steps * 1e3
+    k_ms = sum(kern_ms) / len(kern_ms)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, kernel {k_ms:.3f} ms ({achieved:.1f} TFLOP/s), "
+        f"{info['n_items']} work items")
+
+    result = {
+        "metric": "ragged MLA prefill TFLOP/s (bf16, Dqk192/Dvo128) and % of MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, DeepSeek-V3 MLA prefill shapes)",
+        "config": {"workload": "deepseek_v3_batch", "num_seqs": x.batch,
+                   "tokens": x.qo_indptr[-1], "heads": x.num_heads, "dqk": 192, "dvo": 128,
+                   "causal": True, "sm_scale": x.sm_scale, "seed": 2,
+                   "seq_lens": [b - a for a, b in zip(x.qo_indptr, x.qo_indptr[1:])],
+                   "visible_pairs_per_head": pairs, "flops_per_step": flops,
+                   "work_items": info["n_items"], "block_m": info["block_m"],
+                   "n_xcd": info["n_xcd"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_bf16_kernel",
+                     "kernel_ms": round(k_ms, 4)},
+    }
+    if not args.no_secondary:
+        result["secondary"] = {"merge_state": time_merge(mra, torch, workloads, args.steps,
+                                                         args.warmup)}
+    if args.cpu_seconds > 0:
+        import oracle
+        log("timing the oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(oracle, torch, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

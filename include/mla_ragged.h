@@ -1,0 +1,206 @@
+/*
+ * mla_ragged.h -- C ABI of the MI355X (gfx950) MLA ragged prefill library.
+ *
+ * The operation is DeepSeek-style MLA prefill attention over a ragged batch
+ * (multi-head attention after the latent KV has been decompressed):
+ *   query/key head dim 192 (128 NoPE + 64 RoPE), value/output head dim 128
+ *   ("[DeepseekR1] How ragged prefill manage kv_cache?", sglang issue 3849,
+ *   the question about chunked prefill using MHA with 192/128 dims);
+ *   sequences packed back to back and indexed by qo_indptr / kv_indptr, NHD
+ *   layout, num_kv_heads equal to num_qo_heads, one causal pass over the new
+ *   tokens and one non-causal pass per context chunk, each returning O and
+ *   the per-(token, head) log-sum-exp
+ *   ("vllm.v1.attention.backends.mla.prefill.flashinfer",
+ *   FlashInferPrefillBackend.finalize_attention_metadata and
+ *   FlashInferPrefillImpl.run_prefill_new_tokens / run_prefill_context_chunk);
+ *   the softmax scale is always passed by the caller
+ *   ("[KVCache] PagedKVCache refactor, FlashInfer JIT and MLA integration",
+ *   apache/tvm PR 17674, the sm_scale bullet).
+ *
+ * Definition computed for query row i (0-based within its sequence b) and
+ * head h, with qo_len = qo_indptr[b+1]-qo_indptr[b], kv_len likewise:
+ *   visible keys J = { j : j < kv_len } when not causal, and
+ *   J = { j : j < kv_len - qo_len + i + 1 } when causal (bottom-right
+ *   aligned; this reduces to the usual lower triangle when qo_len == kv_len);
+ *   s_j = sm_scale * <q_i, k_j>;  LSE = ln sum_{j in J} exp(s_j)  (natural log
+ *   of the scaled logits);  O = sum_{j in J} exp(s_j - LSE) v_j.
+ *   A row with J empty gets O = 0 and LSE = -inf.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense, row-major, device pointers unless marked HOST.
+ *    q [Tq, H, 192], k [Tk, H, 192], v [Tk, H, 128], out [Tq, H, 128]
+ *    share one dtype (MLA_DTYPE_BF16 or MLA_DTYPE_FP32); lse [Tq, H] is fp32.
+ *    Device pointers must be 16-byte aligned.
+ *  - The caller owns every tensor and every indptr array; the library never
+ *    frees them. HOST arrays are read only during the call.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued on it and the call returns; device faults surface at the
+ *    caller's next synchronisation, as with any HIP launch.
+ *  - Every call returns MLA_OK or an error status. Arguments are validated on
+ *    the host before any HIP call; an invalid call touches no device state.
+ *    mla_last_error() gives a message for the last failing call of the
+ *    calling thread. No C++ exception crosses this boundary.
+ */
+#ifndef MLA_RAGGED_H
+#define MLA_RAGGED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_DTYPE_BF16 0
+#define MLA_DTYPE_FP32 1
+
+#define MLA_HEAD_DIM_QK 192
+#define MLA_HEAD_DIM_VO 128
+#define MLA_LATENT_DIM 512
+#define MLA_ROPE_DIM 64
+
+enum mla_status {
+    MLA_OK = 0,
+    MLA_EINVAL = 1,       /* bad pointer, size, indptr or scale */
+    MLA_EUNSUPPORTED = 2, /* a dtype or configuration this library does not build */
+    MLA_EHIP = 3,         /* a HIP runtime call failed; see mla_last_error() */
+    MLA_ENOMEM = 4,       /* host or device allocation failed */
+    MLA_ESTATE = 5        /* the plan does not match the call (see mla_ragged_run) */
+};
+
+/* Human-readable name of a status code. Never NULL. */
+const char *mla_status_string(int status);
+
+/* Message for the last failing call on this thread ("" if none). Never NULL. */
+const char *mla_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *mla_version(void);
+
+/*
+ * One-shot ragged prefill: plans the work list from the HOST indptrs, uploads
+ * it and launches the prefill kernel on `stream`.
+ *
+ *   q, k, v      device, NHD (see above), dtype `dtype`.
+ *   qo_indptr    HOST int32 [batch+1]; qo_indptr[0] == 0, non-decreasing;
+ *                qo_indptr[batch] == Tq.
+ *   kv_indptr    HOST int32 [batch+1]; kv_indptr[0] == 0, non-decreasing.
+ *                The pages' causal pass over new tokens uses kv_indptr equal
+ *                to qo_indptr; a context-chunk pass uses that chunk's
+ *                cumulative lengths with causal = 0.
+ *   batch        >= 0 (0 is a no-op). num_heads >= 1.
+ *   causal       0 or 1 (bottom-right aligned, see the definition above).
+ *   sm_scale     finite and > 0; used exactly as given.
+ *   out          device [Tq, H, 128], dtype `dtype`; every row is written.
+ *   lse          device fp32 [Tq, H] natural log, or NULL to skip it.
+ *
+ * Scratch: the work list lives in a library-owned, grow-only device buffer
+ * kept per stream (plus pinned host staging), so calls on different streams
+ * do not share it. Calls on one stream are ordered by that stream.
+ */
+int mla_ragged_prefill(const void *q, const void *k, const void *v,
+                       const int32_t *qo_indptr, const int32_t *kv_indptr,
+                       int32_t batch, int32_t num_heads, int32_t causal, float sm_scale,
+                       int32_t dtype, void *out, float *lse, void *stream);
+
+/*
+ * Plan / run split (the pages plan once per batch and run once per layer:
+ * "vllm.v1.attention.backends.mla.prefill.flashinfer", plan() inside
+ * finalize_attention_metadata versus run() inside run_prefill_new_tokens).
+ */
+typedef struct mla_plan mla_plan;
+
+/* Create an empty plan object (host only, no HIP call). *out receives it. */
+int mla_plan_create(mla_plan **out);
+
+/* Destroy a plan and free its host and device buffers. NULL is a no-op.
+ * The caller must make sure no launched run still reads the plan (for
+ * example by synchronising the stream it ran on). */
+void mla_plan_destroy(mla_plan *plan);
+
+/*
+ * Build the work list on the host: the work partitioner splits every
+ * sequence into query tiles, one work item per (sequence, head, query tile),
+ * ordered so the heaviest groups go first and all tiles of one
+ * (sequence, head) land on the same XCD. Validates like mla_ragged_prefill.
+ * Makes no HIP call, so it also runs on a machine without a GPU.
+ * `dtype` selects the kernel (and so the query-tile height).
+ */
+int mla_ragged_plan(mla_plan *plan, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                    int32_t batch, int32_t num_heads, int32_t causal, int32_t dtype);
+
+/* Copy the planned work list to the plan's device buffer (allocated or grown
+ * on first use) with an asynchronous copy on `stream`, through pinned host
+ * staging. Run the kernel on the same stream (or synchronise first). */
+int mla_plan_upload(mla_plan *plan, void *stream);
+
+/*
+ * Launch the prefill kernel for an uploaded plan. Tensors as for
+ * mla_ragged_prefill; `dtype` must equal the planned dtype and the tensors
+ * must match the planned indptrs (Tq = qo_indptr[batch], Tk = kv_indptr[batch],
+ * num_heads), else MLA_ESTATE. Enqueues exactly one kernel.
+ */
+int mla_ragged_run(const mla_plan *plan, const void *q, const void *k, const void *v,
+                   float sm_scale, int32_t dtype, void *out, float *lse, void *stream);
+
+/*
+ * Work-list inspection (host only): item count, and a copy of the items as
+ * int32 [n, 8] = {q_row0, n_rows, head, kv_start, kv_len, diag0, kv_hi, seq}:
+ *   q_row0   first query token of the tile (global index);
+ *   n_rows   query rows in the tile (0 marks a padding item);
+ *   head     head index;  kv_start first key token of the sequence;
+ *   kv_len   keys in the sequence;
+ *   diag0    row r of the tile sees keys < min(kv_len, max(0, diag0 + r + 1));
+ *   kv_hi    keys the last row of the tile sees (the tile's loop bound);
+ *   seq      sequence index.
+ * `block_m` receives the query-tile height and `n_xcd` the XCD count used.
+ */
+int mla_plan_info(const mla_plan *plan, int64_t *n_items, int32_t *block_m, int32_t *n_xcd);
+int mla_plan_items(const mla_plan *plan, int32_t *dst, int64_t capacity_items);
+
+/* Number of XCDs the partitioner groups work for (default 8, MI355X; 1
+ * turns the grouping off). Applies to later mla_ragged_plan calls. */
+int mla_plan_set_xcds(mla_plan *plan, int32_t n_xcd);
+
+/*
+ * merge_state: combine two attention states computed over disjoint key sets
+ * (the chunked-prefill combine of the causal new-token pass with the
+ * non-causal context-chunk passes; the pages return each pass's (O, LSE)
+ * for this: "vllm.v1.attention.backends.mla.prefill.flashinfer",
+ * run_prefill_context_chunk; sglang issue 3849, forward_return_lse used
+ * for chunked prefill). Per row r:
+ *   lse = ln(e^lse_a[r] + e^lse_b[r]),
+ *   o[r] = e^(lse_a[r]-lse) o_a[r] + e^(lse_b[r]-lse) o_b[r];
+ * a side with lse = -inf has weight 0; both -inf gives o = 0, lse = -inf.
+ *
+ *   o_a, o_b, o  device [num_rows, head_dim] in `dtype` (rows = tokens x heads).
+ *   lse_a, lse_b, lse  device fp32 [num_rows].
+ *   head_dim     must be 128 (the MLA value dim).
+ *   o may alias o_a or o_b and lse may alias lse_a or lse_b (in-place merge).
+ */
+int mla_merge_state(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b,
+                    void *o, float *lse, int64_t num_rows, int32_t head_dim, int32_t dtype,
+                    void *stream);
+
+/*
+ * MLA KV decompression (the question in sglang issue 3849 about
+ * decompressing the 512-dim latent cache for MHA prefill): for every token
+ * t and head h,
+ *   K[t,h,0:128]   = c_kv[t,:] . W_UK[:, h*128:(h+1)*128]
+ *   K[t,h,128:192] = k_rope[t,:]          (shared by all heads)
+ *   V[t,h,0:128]   = c_kv[t,:] . W_UV[:, h*128:(h+1)*128]
+ * bf16 inputs, fp32 accumulation, bf16 outputs.
+ *
+ *   c_kv   device bf16 [T, 512];  k_rope device bf16 [T, 64];
+ *   w_uk, w_uv device bf16 [512, H*128] (column h*128+d is head h, dim d);
+ *   k_out  device bf16 [T, H, 192];  v_out device bf16 [T, H, 128].
+ *   num_tokens >= 0 (0 is a no-op), num_heads >= 1.
+ */
+int mla_decompress_kv(const void *c_kv, const void *k_rope, const void *w_uk, const void *w_uv,
+                      int64_t num_tokens, int32_t num_heads, void *k_out, void *v_out,
+                      void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_RAGGED_H */

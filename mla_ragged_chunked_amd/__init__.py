@@ -1,0 +1,284 @@
+"""MLA ragged prefill for MI355X (gfx950): thin Python binding.
+
+Every call marshals torch tensors into pointers and calls the C ABI declared
+in include/mla_ragged.h; all arithmetic runs in the HIP kernels of
+libmla_ragged.so. PyTorch provides device memory and the current stream
+only. There is no fallback: if the library has not been built, or a tensor
+is not on a GPU, the call raises.
+
+Functions mirror the C entry points:
+  ragged_prefill(q, k, v, qo_indptr, kv_indptr, causal, sm_scale, return_lse=True)
+  merge_state(o_a, lse_a, o_b, lse_b, out=None, out_lse=None)
+  decompress_kv(c_kv, k_rope, w_uk, w_uv, num_heads)
+  Plan: plan() once per batch, run() once per layer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = ["ragged_prefill", "merge_state", "decompress_kv", "Plan", "MlaError", "lib",
+           "LIB_PATH", "DQK", "DVO", "EXPORTED_SYMBOLS"]
+
+DQK, DVO, DLAT, DROPE = 192, 128, 512, 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_ragged.so")
+_BF16, _FP32 = 0, 1
+_DT = {torch.bfloat16: _BF16, torch.float32: _FP32}
+
+EXPORTED_SYMBOLS = [
+    "mla_status_string", "mla_last_error", "mla_version", "mla_ragged_prefill",
+    "mla_plan_create", "mla_plan_destroy", "mla_ragged_plan", "mla_plan_upload",
+    "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_set_xcds",
+    "mla_merge_state", "mla_decompress_kv",
+]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        l = lib()
+        name = l.mla_status_string(status).decode()
+        detail = l.mla_last_error().decode()
+        super().__init__(f"{where}: {name}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    l = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, C = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                         ctypes.c_char_p)
+    sig = {
+        "mla_status_string": ([ctypes.c_int], C),
+        "mla_last_error": ([], C),
+        "mla_version": ([], C),
+        "mla_ragged_prefill": ([P, P, P, P, P, I32, I32, I32, F, I32, P, P, P], ctypes.c_int),
+        "mla_plan_create": ([ctypes.POINTER(P)], ctypes.c_int),
+        "mla_plan_destroy": ([P], None),
+        "mla_ragged_plan": ([P, P, P, I32, I32, I32, I32], ctypes.c_int),
+        "mla_plan_upload": ([P, P], ctypes.c_int),
+        "mla_ragged_run": ([P, P, P, P, F, I32, P, P, P], ctypes.c_int),
+        "mla_plan_info": ([P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32)],
+                          ctypes.c_int),
+        "mla_plan_items": ([P, P, I64], ctypes.c_int),
+        "mla_plan_set_xcds": ([P, I32], ctypes.c_int),
+        "mla_merge_state": ([P, P, P, P, P, P, I64, I32, I32, P], ctypes.c_int),
+        "mla_decompress_kv": ([P, P, P, P, I64, I32, P, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(l, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = l
+    return l
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MlaError(status, where)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _indptr(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _dev_tensor(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Plan:
+    """Work list for one ragged batch: plan once (host), upload, run per layer."""
+
+    def __init__(self, n_xcd: Optional[int] = None):
+        l = lib()
+        h = ctypes.c_void_p()
+        _check(l.mla_plan_create(ctypes.byref(h)), "mla_plan_create")
+        self._h = h
+        self._lib = l
+        if n_xcd is not None:
+            _check(l.mla_plan_set_xcds(h, int(n_xcd)), "mla_plan_set_xcds")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.mla_plan_destroy(h)
+            self._h = None
+
+    def plan(self, qo_indptr, kv_indptr, num_heads: int, causal: bool,
+             dtype: torch.dtype = torch.bfloat16) -> "Plan":
+        qo, kv = _indptr(qo_indptr), _indptr(kv_indptr)
+        if len(qo) != len(kv) or len(qo) < 1:
+            raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+        if dtype not in _DT:
+            raise ValueError("dtype must be torch.bfloat16 or torch.float32")
+        self._qo, self._kv = qo, kv
+        _check(self._lib.mla_ragged_plan(self._h, qo.ctypes.data, kv.ctypes.data, len(qo) - 1,
+                                         int(num_heads), int(bool(causal)), _DT[dtype]),
+               "mla_ragged_plan")
+        self.num_heads, self.causal, self.dtype = int(num_heads), bool(causal), dtype
+        return self
+
+    def upload(self, device=None) -> "Plan":
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        with torch.cuda.device(dev):
+            _check(self._lib.mla_plan_upload(self._h, _stream(dev)), "mla_plan_upload")
+        return self
+
+    def info(self):
+        n, bm, nx = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.mla_plan_info(self._h, ctypes.byref(n), ctypes.byref(bm),
+                                       ctypes.byref(nx)), "mla_plan_info")
+        return {"n_items": n.value, "block_m": bm.value, "n_xcd": nx.value}
+
+    def items(self) -> np.ndarray:
+        n = self.info()["n_items"]
+        buf = np.zeros((max(n, 1), 8), dtype=np.int32)
+        _check(self._lib.mla_plan_items(self._h, buf.ctypes.data, max(n, 1)), "mla_plan_items")
+        return buf[:n]
+
+    def run(self, q, k, v, sm_scale: float, out=None, lse=None, return_lse: bool = True):
+        for t, name in ((q, "q"), (k, "k"), (v, "v")):
+            _dev_tensor(t, name)
+        tq, heads = q.shape[0], q.shape[1]
+        if out is None:
+            out = torch.empty((tq, heads, DVO), dtype=q.dtype, device=q.device)
+        if return_lse and lse is None:
+            lse = torch.empty((tq, heads), dtype=torch.float32, device=q.device)
+        _dev_tensor(out, "out")
+        _check_shapes(q, k, v, out, lse if return_lse else None)
+        with torch.cuda.device(q.device):
+            _check(self._lib.mla_ragged_run(self._h, _ptr(q), _ptr(k), _ptr(v), float(sm_scale),
+                                            _DT[q.dtype], _ptr(out),
+                                            _ptr(lse) if return_lse else None,
+                                            _stream(q.device)),
+                   "mla_ragged_run")
+        return (out, lse) if return_lse else out
+
+
+def _check_shapes(q, k, v, out, lse):
+    if q.dtype not in _DT or not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v, out must share bf16 or fp32")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or out.dim() != 3:
+        raise ValueError("q, k, v, out must be [tokens, heads, dim]")
+    if q.shape[2] != DQK or k.shape[2] != DQK or v.shape[2] != DVO or out.shape[2] != DVO:
+        raise ValueError("head dims must be 192 (q, k) and 128 (v, out)")
+    h = q.shape[1]
+    if k.shape[1] != h or v.shape[1] != h or out.shape[1] != h:
+        raise ValueError("q, k, v, out must have the same number of heads")
+    if k.shape[0] != v.shape[0] or out.shape[0] != q.shape[0]:
+        raise ValueError("token counts of k/v or q/out differ")
+    if lse is not None:
+        _dev_tensor(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[0], h):
+            raise ValueError("lse must be fp32 [tokens, heads]")
+
+
+def ragged_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qo_indptr, kv_indptr,
+                   causal: bool, sm_scale: float, return_lse: bool = True,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Ragged MLA prefill. q [Tq,H,192], k [Tk,H,192], v [Tk,H,128] on the GPU;
+    host int indptrs of length batch+1. Returns out [Tq,H,128] (and lse [Tq,H]
+    fp32, natural log) on the current stream."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, name)
+    qo, kv = _indptr(qo_indptr), _indptr(kv_indptr)
+    if len(qo) != len(kv) or len(qo) < 1:
+        raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+    if qo[-1] != q.shape[0] or kv[-1] != k.shape[0]:
+        raise ValueError("indptr totals do not match the token counts of q / k")
+    tq, heads = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((tq, heads, DVO), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((tq, heads), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, "out")
+    _check_shapes(q, k, v, out, lse if return_lse else None)
+    l = lib()
+    with torch.cuda.device(q.device):
+        _check(l.mla_ragged_prefill(_ptr(q), _ptr(k), _ptr(v), qo.ctypes.data, kv.ctypes.data,
+                                    len(qo) - 1, heads, int(bool(causal)), float(sm_scale),
+                                    _DT[q.dtype], _ptr(out), _ptr(lse) if return_lse else None,
+                                    _stream(q.device)),
+               "mla_ragged_prefill")
+    return (out, lse) if return_lse else out
+
+
+def merge_state(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+                out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None):
+    """Merge two (O, LSE) states over disjoint key sets. o_* [..., 128]
+    (bf16 or fp32), lse_* [...] fp32. out/out_lse may alias the inputs."""
+    for t, name in ((o_a, "o_a"), (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
+        _dev_tensor(t, name)
+    if o_a.shape != o_b.shape or lse_a.shape != lse_b.shape or o_a.shape[:-1] != lse_a.shape:
+        raise ValueError("state shapes differ")
+    if o_a.dtype != o_b.dtype or o_a.dtype not in _DT:
+        raise ValueError("o_a and o_b must share bf16 or fp32")
+    if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise ValueError("lse must be fp32")
+    if out is None:
+        out = torch.empty_like(o_a)
+    if out_lse is None:
+        out_lse = torch.empty_like(lse_a)
+    _dev_tensor(out, "out")
+    _dev_tensor(out_lse, "out_lse")
+    if out.shape != o_a.shape or out.dtype != o_a.dtype or out_lse.shape != lse_a.shape:
+        raise ValueError("output shapes differ from the inputs")
+    rows = lse_a.numel()
+    with torch.cuda.device(o_a.device):
+        _check(lib().mla_merge_state(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out),
+                                     _ptr(out_lse), rows, o_a.shape[-1], _DT[o_a.dtype],
+                                     _stream(o_a.device)),
+               "mla_merge_state")
+    return out, out_lse
+
+
+def decompress_kv(c_kv: torch.Tensor, k_rope: torch.Tensor, w_uk: torch.Tensor,
+                  w_uv: torch.Tensor, num_heads: int, k_out=None, v_out=None):
+    """K [T,H,192] = [c_kv W_UK | k_rope], V [T,H,128] = c_kv W_UV (bf16)."""
+    for t, name in ((c_kv, "c_kv"), (k_rope, "k_rope"), (w_uk, "w_uk"), (w_uv, "w_uv")):
+        _dev_tensor(t, name)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    t = c_kv.shape[0]
+    if c_kv.shape != (t, DLAT) or k_rope.shape != (t, DROPE):
+        raise ValueError("c_kv must be [T,512] and k_rope [T,64]")
+    if w_uk.shape != (DLAT, num_heads * 128) or w_uv.shape != (DLAT, num_heads * DVO):
+        raise ValueError("w_uk / w_uv must be [512, H*128]")
+    if k_out is None:
+        k_out = torch.empty((t, num_heads, DQK), dtype=torch.bfloat16, device=c_kv.device)
+    if v_out is None:
+        v_out = torch.empty((t, num_heads, DVO), dtype=torch.bfloat16, device=c_kv.device)
+    _dev_tensor(k_out, "k_out")
+    _dev_tensor(v_out, "v_out")
+    with torch.cuda.device(c_kv.device):
+        _check(lib().mla_decompress_kv(_ptr(c_kv), _ptr(k_rope), _ptr(w_uk), _ptr(w_uv), t,
+                                       int(num_heads), _ptr(k_out), _ptr(v_out),
+                                       _stream(c_kv.device)),
+               "mla_decompress_kv")
+    return k_out, v_out

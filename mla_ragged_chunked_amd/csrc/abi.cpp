@@ -1,0 +1,393 @@
+// C ABI of the MLA ragged prefill library: argument validation, plans,
+// per-stream scratch for the one-shot call, and kernel dispatch.
+//
+// Every public function validates on the host before its first HIP call and
+// returns a status; messages go to a thread-local buffer read by
+// mla_last_error(). No exception escapes.
+#include "../../include/mla_ragged.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using mla::WorkItem;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+    g_last_error = msg;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    std::string m = std::string(what) + ": " + hipGetErrorString(e);
+    return fail(MLA_EHIP, m);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Pinned host staging + device buffer for one work list. Grow-only.
+// A ring of pinned slots lets several uploads be in flight on a stream
+// before the host has to wait for the oldest copy to finish.
+struct DeviceWorkList {
+    static constexpr int kRing = 4;
+    WorkItem* dev = nullptr;
+    size_t dev_cap = 0;             // items
+    int device = -1;
+    WorkItem* pinned[kRing] = {};
+    size_t pinned_cap[kRing] = {};
+    hipEvent_t done[kRing] = {};
+    bool pending[kRing] = {};
+    int next = 0;
+
+    ~DeviceWorkList() { release(); }
+
+    void release() {
+        for (int i = 0; i < kRing; ++i) {
+            if (pending[i]) (void)hipEventSynchronize(done[i]);
+            if (done[i]) (void)hipEventDestroy(done[i]);
+            if (pinned[i]) (void)hipHostFree(pinned[i]);
+            done[i] = nullptr;
+            pinned[i] = nullptr;
+            pinned_cap[i] = 0;
+            pending[i] = false;
+        }
+        if (dev) (void)hipFree(dev);
+        dev = nullptr;
+        dev_cap = 0;
+    }
+
+    // Asynchronously copy `items` to `dev` on `stream`.
+    int upload(const std::vector<WorkItem>& items, hipStream_t stream) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        if (device != -1 && device != cur) {
+            // the plan moves to another device: drop the old buffers
+            int keep = cur;
+            (void)hipSetDevice(device);
+            release();
+            (void)hipSetDevice(keep);
+        }
+        device = cur;
+        const size_t n = items.empty() ? 1 : items.size();
+        if (dev_cap < n) {
+            if (dev) {
+                // a previous run on some stream may still read the old buffer
+                e = hipDeviceSynchronize();
+                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+                (void)hipFree(dev);
+                dev = nullptr;
+                dev_cap = 0;
+            }
+            e = hipMalloc(&dev, n * sizeof(WorkItem));
+            if (e != hipSuccess) { dev = nullptr; return fail(MLA_ENOMEM, "hipMalloc of the work list failed"); }
+            dev_cap = n;
+        }
+        if (items.empty()) return MLA_OK;
+        const int slot = next;
+        next = (next + 1) % kRing;
+        if (pending[slot]) {
+            e = hipEventSynchronize(done[slot]);
+            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            pending[slot] = false;
+        }
+        if (pinned_cap[slot] < items.size()) {
+            if (pinned[slot]) (void)hipHostFree(pinned[slot]);
+            pinned[slot] = nullptr;
+            pinned_cap[slot] = 0;
+            e = hipHostMalloc(reinterpret_cast<void**>(&pinned[slot]), items.size() * sizeof(WorkItem),
+                              hipHostMallocDefault);
+            if (e != hipSuccess) { pinned[slot] = nullptr; return fail(MLA_ENOMEM, "hipHostMalloc of staging failed"); }
+            pinned_cap[slot] = items.size();
+        }
+        if (!done[slot]) {
+            e = hipEventCreateWithFlags(&done[slot], hipEventDisableTiming);
+            if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        }
+        std::memcpy(pinned[slot], items.data(), items.size() * sizeof(WorkItem));
+        e = hipMemcpyAsync(dev, pinned[slot], items.size() * sizeof(WorkItem),
+                           hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of the work list");
+        e = hipEventRecord(done[slot], stream);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        pending[slot] = true;
+        return MLA_OK;
+    }
+};
+
+}  // namespace
+
+struct mla_plan {
+    std::vector<WorkItem> items;
+    int64_t tq = 0, tk = 0;
+    int32_t batch = 0, num_heads = 0, causal = 0, dtype = -1, block_m = 0;
+    int32_t n_xcd = 8;
+    bool planned = false;
+    bool uploaded = false;
+    DeviceWorkList dwl;
+};
+
+namespace {
+
+int check_dtype(int32_t dtype) {
+    if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_FP32)
+        return fail(MLA_EUNSUPPORTED, "dtype must be MLA_DTYPE_BF16 or MLA_DTYPE_FP32");
+    return MLA_OK;
+}
+
+int check_scale(float sm_scale) {
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(MLA_EINVAL, "sm_scale must be finite and > 0");
+    return MLA_OK;
+}
+
+int check_tensors(const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, int64_t tq, int64_t tk) {
+    if (tq > 0 && (q == nullptr || out == nullptr))
+        return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
+    if (tk > 0 && (k == nullptr || v == nullptr))
+        return fail(MLA_EINVAL, "k and v must be non-NULL when there are keys");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(MLA_EINVAL, "q, k, v and out must be 16-byte aligned");
+    if (!aligned16(lse) && lse != nullptr)
+        return fail(MLA_EINVAL, "lse must be 16-byte aligned");
+    return MLA_OK;
+}
+
+int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, int32_t heads,
+            int32_t causal, int32_t dtype) {
+    if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    p->planned = false;
+    p->uploaded = false;
+    if (int s = check_dtype(dtype)) return s;
+    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
+    if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
+    if (heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
+    if (batch > 0 && (qo == nullptr || kv == nullptr)) return fail(MLA_EINVAL, "indptr is NULL");
+    const int bm = dtype == MLA_DTYPE_BF16 ? mla::kBf16BlockM : mla::kFp32BlockM;
+    std::string err;
+    try {
+        if (!mla::build_work_list(qo, kv, batch, heads, causal != 0, bm, p->n_xcd, p->items, err))
+            return fail(MLA_EINVAL, err);
+    } catch (const std::bad_alloc&) {
+        return fail(MLA_ENOMEM, "host allocation of the work list failed");
+    }
+    // 32-bit token indices inside the kernels: Tq*H and Tk*H row counts must fit
+    const int64_t tq = batch > 0 ? qo[batch] : 0;
+    const int64_t tk = batch > 0 ? kv[batch] : 0;
+    if (tq * heads > INT32_MAX || tk * heads > INT32_MAX)
+        return fail(MLA_EUNSUPPORTED, "tokens x heads exceeds 2^31 rows");
+    p->tq = tq;
+    p->tk = tk;
+    p->batch = batch;
+    p->num_heads = heads;
+    p->causal = causal;
+    p->dtype = dtype;
+    p->block_m = bm;
+    p->planned = true;
+    return MLA_OK;
+}
+
+int do_run(const mla_plan* p, const void* q, const void* k, const void* v, float sm_scale,
+           int32_t dtype, void* out, float* lse, hipStream_t stream) {
+    if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (!p->planned) return fail(MLA_ESTATE, "plan has not been built");
+    if (!p->uploaded) return fail(MLA_ESTATE, "plan has not been uploaded (mla_plan_upload)");
+    if (dtype != p->dtype) return fail(MLA_ESTATE, "dtype differs from the planned dtype");
+    if (int s = check_scale(sm_scale)) return s;
+    if (int s = check_tensors(q, k, v, out, lse, p->tq, p->tk)) return s;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != p->dwl.device) return fail(MLA_ESTATE, "plan was uploaded on another device");
+    if (p->items.empty()) return MLA_OK;
+    const int64_t n = static_cast<int64_t>(p->items.size());
+    e = dtype == MLA_DTYPE_BF16
+            ? mla::launch_prefill_bf16(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale, stream)
+            : mla::launch_prefill_fp32(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale, stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return MLA_OK;
+}
+
+// One-shot calls keep one plan per (device, stream).
+std::mutex g_oneshot_mu;
+std::map<std::pair<int, void*>, mla_plan*>* g_oneshot = nullptr;
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+    switch (status) {
+        case MLA_OK: return "MLA_OK";
+        case MLA_EINVAL: return "MLA_EINVAL";
+        case MLA_EUNSUPPORTED: return "MLA_EUNSUPPORTED";
+        case MLA_EHIP: return "MLA_EHIP";
+        case MLA_ENOMEM: return "MLA_ENOMEM";
+        case MLA_ESTATE: return "MLA_ESTATE";
+        default: return "MLA_UNKNOWN_STATUS";
+    }
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+const char* mla_version(void) { return "0.1.0"; }
+
+int mla_plan_create(mla_plan** out) {
+    if (out == nullptr) return fail(MLA_EINVAL, "out is NULL");
+    *out = new (std::nothrow) mla_plan();
+    if (*out == nullptr) return fail(MLA_ENOMEM, "plan allocation failed");
+    return MLA_OK;
+}
+
+void mla_plan_destroy(mla_plan* plan) { delete plan; }
+
+int mla_plan_set_xcds(mla_plan* plan, int32_t n_xcd) {
+    if (plan == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (n_xcd < 1 || n_xcd > 64) return fail(MLA_EINVAL, "n_xcd must be in [1, 64]");
+    plan->n_xcd = n_xcd;
+    return MLA_OK;
+}
+
+int mla_ragged_plan(mla_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    int32_t batch, int32_t num_heads, int32_t causal, int32_t dtype) {
+    return do_plan(plan, qo_indptr, kv_indptr, batch, num_heads, causal, dtype);
+}
+
+int mla_plan_upload(mla_plan* plan, void* stream) {
+    if (plan == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
+    int s = plan->dwl.upload(plan->items, static_cast<hipStream_t>(stream));
+    if (s != MLA_OK) return s;
+    plan->uploaded = true;
+    return MLA_OK;
+}
+
+int mla_ragged_run(const mla_plan* plan, const void* q, const void* k, const void* v,
+                   float sm_scale, int32_t dtype, void* out, float* lse, void* stream) {
+    return do_run(plan, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream));
+}
+
+int mla_plan_info(const mla_plan* plan, int64_t* n_items, int32_t* block_m, int32_t* n_xcd) {
+    if (plan == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
+    if (n_items) *n_items = static_cast<int64_t>(plan->items.size());
+    if (block_m) *block_m = plan->block_m;
+    if (n_xcd) *n_xcd = plan->n_xcd;
+    return MLA_OK;
+}
+
+int mla_plan_items(const mla_plan* plan, int32_t* dst, int64_t capacity_items) {
+    if (plan == nullptr || dst == nullptr) return fail(MLA_EINVAL, "plan or dst is NULL");
+    if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
+    if (capacity_items < static_cast<int64_t>(plan->items.size()))
+        return fail(MLA_EINVAL, "capacity is smaller than the item count");
+    std::memcpy(dst, plan->items.data(), plan->items.size() * sizeof(WorkItem));
+    return MLA_OK;
+}
+
+int mla_ragged_prefill(const void* q, const void* k, const void* v, const int32_t* qo_indptr,
+                       const int32_t* kv_indptr, int32_t batch, int32_t num_heads,
+                       int32_t causal, float sm_scale, int32_t dtype, void* out, float* lse,
+                       void* stream) {
+    // validate everything before the first HIP call
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_scale(sm_scale)) return s;
+    if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
+    if (num_heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
+    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
+    if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
+        return fail(MLA_EINVAL, "indptr is NULL");
+    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
+    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
+    if (int s = check_tensors(q, k, v, out, lse, tq, tk)) return s;
+    mla_plan scratch_check;
+    if (int s = do_plan(&scratch_check, qo_indptr, kv_indptr, batch, num_heads, causal, dtype))
+        return s;
+    if (scratch_check.items.empty()) return MLA_OK;
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    mla_plan* p = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_oneshot_mu);
+        if (g_oneshot == nullptr) g_oneshot = new (std::nothrow) std::map<std::pair<int, void*>, mla_plan*>();
+        if (g_oneshot == nullptr) return fail(MLA_ENOMEM, "one-shot plan table");
+        auto key = std::make_pair(dev, stream);
+        auto it = g_oneshot->find(key);
+        if (it == g_oneshot->end()) {
+            p = new (std::nothrow) mla_plan();
+            if (p == nullptr) return fail(MLA_ENOMEM, "one-shot plan");
+            (*g_oneshot)[key] = p;
+        } else {
+            p = it->second;
+        }
+    }
+    // Calls on one stream are serialised by the caller's stream order; the
+    // host-side plan object is per (device, stream), so a thread per stream
+    // never shares it.
+    p->items.swap(scratch_check.items);
+    p->tq = scratch_check.tq;
+    p->tk = scratch_check.tk;
+    p->batch = batch;
+    p->num_heads = num_heads;
+    p->causal = causal;
+    p->dtype = dtype;
+    p->block_m = scratch_check.block_m;
+    p->planned = true;
+    p->uploaded = false;
+    if (int s = mla_plan_upload(p, stream)) return s;
+    return do_run(p, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream));
+}
+
+int mla_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o, float* lse, int64_t num_rows, int32_t head_dim, int32_t dtype,
+                    void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (head_dim != MLA_HEAD_DIM_VO) return fail(MLA_EUNSUPPORTED, "head_dim must be 128");
+    if (num_rows < 0) return fail(MLA_EINVAL, "num_rows must be >= 0");
+    if (num_rows == 0) return MLA_OK;
+    if (num_rows > INT32_MAX) return fail(MLA_EUNSUPPORTED, "num_rows exceeds 2^31");
+    if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse)
+        return fail(MLA_EINVAL, "merge_state pointers must be non-NULL");
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o) || !aligned16(lse_a) ||
+        !aligned16(lse_b) || !aligned16(lse))
+        return fail(MLA_EINVAL, "merge_state pointers must be 16-byte aligned");
+    hipError_t e = mla::launch_merge(o_a, lse_a, o_b, lse_b, o, lse, num_rows,
+                                     dtype == MLA_DTYPE_BF16 ? 1 : 0,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return MLA_OK;
+}
+
+int mla_decompress_kv(const void* c_kv, const void* k_rope, const void* w_uk, const void* w_uv,
+                      int64_t num_tokens, int32_t num_heads, void* k_out, void* v_out,
+                      void* stream) {
+    if (num_tokens < 0) return fail(MLA_EINVAL, "num_tokens must be >= 0");
+    if (num_heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
+    if (num_tokens == 0) return MLA_OK;
+    if (num_tokens * num_heads > INT32_MAX)
+        return fail(MLA_EUNSUPPORTED, "tokens x heads exceeds 2^31 rows");
+    if (!c_kv || !k_rope || !w_uk || !w_uv || !k_out || !v_out)
+        return fail(MLA_EINVAL, "decompression pointers must be non-NULL");
+    if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) || !aligned16(w_uv) ||
+        !aligned16(k_out) || !aligned16(v_out))
+        return fail(MLA_EINVAL, "decompression pointers must be 16-byte aligned");
+    hipError_t e = mla::launch_decompress(c_kv, k_rope, w_uk, w_uv, num_tokens, num_heads, k_out,
+                                          v_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decompression kernel launch");
+    return MLA_OK;
+}
+
+}  // extern "C"

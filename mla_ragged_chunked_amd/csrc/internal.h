@@ -1,0 +1,59 @@
+// Internal declarations shared by the C ABI, the planner and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace mla {
+
+constexpr int kDqk = 192;
+constexpr int kDvo = 128;
+constexpr int kDlat = 512;
+constexpr int kDrope = 64;
+constexpr int kDnope = 128;
+
+// One work item = one query tile of one (sequence, head). 32 bytes.
+//   row r of the tile (0 <= r < n_rows) sees keys [0, lim(r)) of its sequence,
+//   lim(r) = min(kv_len, max(0, diag0 + r + 1)).
+// Non-causal tiles carry diag0 = kv_len, so lim(r) = kv_len.
+struct WorkItem {
+    int32_t q_row0;    // global token index of the tile's first query row
+    int32_t n_rows;    // rows in the tile; 0 = padding item (kernel returns)
+    int32_t head;
+    int32_t kv_start;  // global token index of the sequence's first key
+    int32_t kv_len;
+    int32_t diag0;
+    int32_t kv_hi;     // lim(n_rows - 1): keys the tile must visit
+    int32_t seq;
+};
+static_assert(sizeof(WorkItem) == 32, "work item layout");
+
+// Query-tile heights of the two prefill kernels.
+constexpr int kBf16BlockM = 256;   // 4 waves x 64 rows
+constexpr int kFp32BlockM = 64;    // 1 wave  x 64 rows
+
+// Build the ordered work list (host only). Returns false with `err` set on
+// invalid input. `block_m` is the query-tile height, `n_xcd` the number of
+// XCDs work is grouped for (1 = no grouping).
+bool build_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                     int num_heads, bool causal, int block_m, int n_xcd,
+                     std::vector<WorkItem>& out, std::string& err);
+
+// Kernel launchers (one kernel each, enqueued on `stream`).
+hipError_t launch_prefill_bf16(const WorkItem* items, int64_t n_items, const void* q,
+                               const void* k, const void* v, void* out, float* lse,
+                               int num_heads, float sm_scale, hipStream_t stream);
+hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const void* q,
+                               const void* k, const void* v, void* out, float* lse,
+                               int num_heads, float sm_scale, hipStream_t stream);
+hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b,
+                        const float* lse_b, void* o, float* lse, int64_t num_rows,
+                        int dtype_bf16, hipStream_t stream);
+hipError_t launch_decompress(const void* c_kv, const void* k_rope, const void* w_uk,
+                             const void* w_uv, int64_t num_tokens, int num_heads,
+                             void* k_out, void* v_out, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,130 @@
+// Work partitioner for ragged prefill (host only, no HIP calls).
+//
+// The pages plan once per batch from qo_indptr / kv_indptr and run once per
+// layer ("vllm.v1.attention.backends.mla.prefill.flashinfer",
+// finalize_attention_metadata: plan() with kv_indptr = qo_indptr for the
+// causal pass and kv_indptr = cu_seq_lens[i] for each context chunk).
+// This partitioner turns those indptrs into one work item per
+// (sequence, head, query tile), ordered for the MI355X:
+//
+//  1. A tile of `block_m` query rows needs keys [0, kv_hi) of its sequence,
+//     kv_hi from the bottom-right causal rule (or kv_len when non-causal);
+//     its cost is kv_hi plus a fixed charge for loading Q and writing O.
+//  2. All tiles of one (sequence, head) form a group: they read the same K/V
+//     rows, so they should share one XCD's L2. Groups are dealt to the XCD
+//     bins heaviest first, each to the currently lightest bin (LPT).
+//  3. Each bin lists its groups heaviest first and, inside a group, its
+//     tiles heaviest first, so long tiles start early and the tail is short.
+//  4. The hardware hands workgroup i to XCD i mod n_xcd, so bin x's s-th item
+//     is placed at index s * n_xcd + x; shorter bins are padded with
+//     empty items (n_rows = 0) that the kernel skips.
+#include <algorithm>
+#include <numeric>
+
+#include "internal.h"
+
+namespace mla {
+
+namespace {
+constexpr int64_t kTileFixedCost = 64;   // Q load + epilogue, in key-equivalents
+
+struct Tile {
+    int32_t q_row0, n_rows, kv_start, kv_len, diag0, kv_hi, seq;
+    int64_t cost;
+};
+}  // namespace
+
+bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_heads,
+                     bool causal, int block_m, int n_xcd, std::vector<WorkItem>& out,
+                     std::string& err) {
+    out.clear();
+    if (batch < 0) { err = "batch must be >= 0"; return false; }
+    if (num_heads < 1 || num_heads > 65535) { err = "num_heads must be in [1, 65535]"; return false; }
+    if (block_m < 1) { err = "block_m must be >= 1"; return false; }
+    if (n_xcd < 1 || n_xcd > 64) { err = "n_xcd must be in [1, 64]"; return false; }
+    if (batch == 0) return true;
+    if (qo == nullptr || kv == nullptr) { err = "indptr pointer is NULL"; return false; }
+    if (qo[0] != 0 || kv[0] != 0) { err = "indptr[0] must be 0"; return false; }
+    for (int b = 0; b < batch; ++b) {
+        if (qo[b + 1] < qo[b]) { err = "qo_indptr must be non-decreasing"; return false; }
+        if (kv[b + 1] < kv[b]) { err = "kv_indptr must be non-decreasing"; return false; }
+    }
+
+    // Tiles of every sequence (shared by all heads).
+    std::vector<Tile> tiles;
+    std::vector<std::pair<size_t, size_t>> seq_tiles(batch);   // [begin, end) into tiles
+    for (int b = 0; b < batch; ++b) {
+        const int32_t qo_len = qo[b + 1] - qo[b];
+        const int32_t kv_len = kv[b + 1] - kv[b];
+        const size_t begin = tiles.size();
+        for (int32_t r0 = 0; r0 < qo_len; r0 += block_m) {
+            Tile t;
+            t.q_row0 = qo[b] + r0;
+            t.n_rows = std::min(block_m, qo_len - r0);
+            t.kv_start = kv[b];
+            t.kv_len = kv_len;
+            // row r sees keys < kv_len - qo_len + (r0 + r) + 1 when causal
+            t.diag0 = causal ? kv_len - qo_len + r0 : kv_len;
+            const int64_t lim_last = static_cast<int64_t>(t.diag0) + t.n_rows;
+            t.kv_hi = static_cast<int32_t>(std::min<int64_t>(kv_len, std::max<int64_t>(0, lim_last)));
+            t.seq = b;
+            t.cost = t.kv_hi + kTileFixedCost;
+            tiles.push_back(t);
+        }
+        seq_tiles[b] = {begin, tiles.size()};
+        // heaviest tile first inside the sequence
+        std::stable_sort(tiles.begin() + begin, tiles.end(),
+                         [](const Tile& a, const Tile& c) { return a.cost > c.cost; });
+    }
+    if (tiles.empty()) return true;
+
+    // Groups = (sequence, head), all heads of a sequence cost the same.
+    struct Group { int32_t seq, head; int64_t cost; };
+    std::vector<Group> groups;
+    groups.reserve(static_cast<size_t>(batch) * num_heads);
+    for (int b = 0; b < batch; ++b) {
+        if (seq_tiles[b].first == seq_tiles[b].second) continue;
+        int64_t c = 0;
+        for (size_t i = seq_tiles[b].first; i < seq_tiles[b].second; ++i) c += tiles[i].cost;
+        for (int h = 0; h < num_heads; ++h) groups.push_back({b, h, c});
+    }
+    std::stable_sort(groups.begin(), groups.end(),
+                     [](const Group& a, const Group& c) { return a.cost > c.cost; });
+
+    // LPT deal into XCD bins.
+    std::vector<std::vector<const Group*>> bins(n_xcd);
+    std::vector<int64_t> load(n_xcd, 0);
+    std::vector<size_t> count(n_xcd, 0);
+    for (const Group& g : groups) {
+        int best = 0;
+        for (int x = 1; x < n_xcd; ++x)
+            if (load[x] < load[best]) best = x;
+        bins[best].push_back(&g);
+        load[best] += g.cost;
+        count[best] += seq_tiles[g.seq].second - seq_tiles[g.seq].first;
+    }
+    const size_t slots = *std::max_element(count.begin(), count.end());
+
+    WorkItem pad{};
+    out.assign(slots * static_cast<size_t>(n_xcd), pad);
+    for (int x = 0; x < n_xcd; ++x) {
+        size_t s = 0;
+        for (const Group* g : bins[x]) {
+            for (size_t i = seq_tiles[g->seq].first; i < seq_tiles[g->seq].second; ++i, ++s) {
+                const Tile& t = tiles[i];
+                WorkItem& w = out[s * n_xcd + x];
+                w.q_row0 = t.q_row0;
+                w.n_rows = t.n_rows;
+                w.head = g->head;
+                w.kv_start = t.kv_start;
+                w.kv_len = t.kv_len;
+                w.diag0 = t.diag0;
+                w.kv_hi = t.kv_hi;
+                w.seq = t.seq;
+            }
+        }
+    }
+    return true;
+}
+
+}  // namespace mla

@@ -1,0 +1,193 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects invalid arguments with a status before touching the
+device, and its work partitioner covers every (sequence, head, row) once."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import mla_ragged_chunked_amd as mra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_ragged.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_lists():
+    assert _declared() == sorted(mra.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", mra.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [s for s in _declared() if s not in exported]
+    assert not missing, f"not exported: {missing}"
+    lib = mra.lib()
+    for s in _declared():
+        assert getattr(lib, s) is not None
+
+
+def test_status_strings_and_version():
+    lib = mra.lib()
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_status_string(1) == b"MLA_EINVAL"
+    assert lib.mla_status_string(99) == b"MLA_UNKNOWN_STATUS"
+    assert lib.mla_version().decode().count(".") == 2
+
+
+def _prefill(**kw):
+    lib = mra.lib()
+    qo = np.asarray(kw.pop("qo", [0, 4]), dtype=np.int32)
+    kv = np.asarray(kw.pop("kv", [0, 4]), dtype=np.int32)
+    args = dict(q=16, k=16, v=16, batch=len(qo) - 1, heads=2, causal=1, scale=0.1, dtype=0,
+                out=16, lse=16)
+    args.update(kw)
+    return lib.mla_ragged_prefill(args["q"], args["k"], args["v"], qo.ctypes.data,
+                                  kv.ctypes.data, args["batch"], args["heads"], args["causal"],
+                                  args["scale"], args["dtype"], args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 2),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(scale=-1.0), 1),
+    (dict(heads=0), 1),
+    (dict(causal=2), 1),
+    (dict(batch=-1), 1),
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(k=None), 1),
+    (dict(q=24), 1),                       # misaligned
+    (dict(lse=8), 1),                      # misaligned lse
+    (dict(qo=[1, 4], kv=[0, 4]), 1),       # indptr[0] != 0
+    (dict(qo=[0, 4, 2], kv=[0, 4, 5]), 1),  # decreasing
+    (dict(qo=[0, 4], kv=[0, 4, 8][:2], heads=70000), 1),
+])
+def test_prefill_rejects_invalid_arguments(kw, status):
+    assert _prefill(**kw) == status
+    assert len(mra.lib().mla_last_error()) > 0
+
+
+def test_empty_batch_is_a_no_op():
+    assert _prefill(qo=[0], kv=[0], q=None, k=None, v=None, out=None, lse=None) == 0
+
+
+def test_merge_and_decompress_reject_invalid_arguments():
+    lib = mra.lib()
+    assert lib.mla_merge_state(16, 16, 16, 16, 16, 16, 10, 64, 0, None) == 2    # head_dim
+    assert lib.mla_merge_state(16, 16, 16, 16, 16, 16, 10, 128, 5, None) == 2   # dtype
+    assert lib.mla_merge_state(16, 16, None, 16, 16, 16, 10, 128, 0, None) == 1
+    assert lib.mla_merge_state(16, 16, 16, 16, 16, 20, 10, 128, 0, None) == 1   # misaligned
+    assert lib.mla_merge_state(16, 16, 16, 16, 16, 16, -1, 128, 0, None) == 1
+    assert lib.mla_merge_state(None, None, None, None, None, None, 0, 128, 0, None) == 0
+    assert lib.mla_decompress_kv(16, 16, 16, 16, 10, 0, 16, 16, None) == 1
+    assert lib.mla_decompress_kv(16, 16, None, 16, 10, 2, 16, 16, None) == 1
+    assert lib.mla_decompress_kv(16, 16, 16, 16, -5, 2, 16, 16, None) == 1
+    assert lib.mla_decompress_kv(None, None, None, None, 0, 2, None, None, None) == 0
+
+
+def test_run_before_upload_is_a_state_error():
+    p = mra.Plan()
+    lib = mra.lib()
+    assert lib.mla_ragged_run(p._h, 16, 16, 16, 0.1, 0, 16, 16, None) == 5
+    p.plan([0, 4], [0, 4], 2, True)
+    assert lib.mla_ragged_run(p._h, 16, 16, 16, 0.1, 0, 16, 16, None) == 5   # not uploaded
+
+
+# ---------------------------------------------------------------------------
+# work partitioner
+# ---------------------------------------------------------------------------
+
+def _lim(r, diag0, kv_len):
+    return min(kv_len, max(0, diag0 + r + 1))
+
+
+def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8):
+    import torch
+    p = mra.Plan(n_xcd=n_xcd)
+    p.plan(qo, kv, heads, causal, torch.bfloat16 if dtype_name == "bf16" else torch.float32)
+    info = p.info()
+    items = p.items()
+    bm = info["block_m"]
+    real = items[items[:, 1] > 0]
+    # every (token, head) exactly once
+    cover = np.zeros((qo[-1], heads), dtype=np.int64)
+    for (q_row0, n_rows, head, kv_start, kv_len, diag0, kv_hi, seq) in real:
+        assert 0 < n_rows <= bm
+        assert qo[seq] <= q_row0 and q_row0 + n_rows <= qo[seq + 1]     # inside its sequence
+        assert (q_row0 - qo[seq]) % bm == 0
+        assert kv_start == kv[seq] and kv_len == kv[seq + 1] - kv[seq]
+        qo_len = qo[seq + 1] - qo[seq]
+        r0 = q_row0 - qo[seq]
+        want_diag0 = kv_len - qo_len + r0 if causal else kv_len
+        assert diag0 == want_diag0
+        assert kv_hi == _lim(n_rows - 1, diag0, kv_len)
+        cover[q_row0:q_row0 + n_rows, head] += 1
+    assert np.all(cover == 1)
+    # XCD grouping: all tiles of one (sequence, head) share index mod n_xcd
+    idx = np.nonzero(items[:, 1] > 0)[0]
+    groups = {}
+    for i in idx:
+        key = (items[i, 7], items[i, 2])
+        groups.setdefault(key, set()).add(i % n_xcd)
+    assert all(len(v) == 1 for v in groups.values())
+    assert len(items) % n_xcd == 0
+    return items, info
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_partition_covers_every_row_once(causal):
+    lens = [1, 17, 64, 300, 257, 0, 1000]
+    qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    _check_plan(qo, qo, 3, causal)
+
+
+def test_partition_handles_ragged_edges():
+    # qo > kv (rows with no visible key), kv = 0, qo = 0, kv > qo
+    qo_lens = [5, 300, 0, 7, 513]
+    kv_lens = [2, 0, 9, 40, 513]
+    qo = np.concatenate([[0], np.cumsum(qo_lens)]).astype(np.int32)
+    kv = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
+    items, _ = _check_plan(qo, kv, 2, True)
+    # the tile of the kv = 0 sequence has nothing to visit
+    s1 = items[(items[:, 7] == 1) & (items[:, 1] > 0)]
+    assert np.all(s1[:, 6] == 0)
+    _check_plan(qo, kv, 2, False, dtype_name="fp32")
+
+
+def test_partition_balances_xcds_and_orders_heaviest_first():
+    lens = [16, 32768, 40, 5000, 2000, 100, 8191, 3]
+    qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    items, info = _check_plan(qo, qo, 16, True)
+    cost = np.where(items[:, 1] > 0, items[:, 6] + 64, 0).astype(np.int64)
+    per_xcd = [cost[x::8].sum() for x in range(8)]
+    group_cost = {}
+    for it, c in zip(items, cost):
+        if it[1] > 0:
+            group_cost[(it[7], it[2])] = group_cost.get((it[7], it[2]), 0) + c
+    assert max(per_xcd) - min(per_xcd) <= max(group_cost.values())
+    # inside one XCD queue the groups come heaviest first
+    for x in range(8):
+        seen = []
+        for it in items[x::8]:
+            if it[1] > 0 and (not seen or seen[-1] != (it[7], it[2])):
+                seen.append((it[7], it[2]))
+        costs = [group_cost[k] for k in seen]
+        assert costs == sorted(costs, reverse=True)
+
+
+def test_partition_without_xcd_grouping_has_no_padding():
+    lens = [100, 700, 3]
+    qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    items, info = _check_plan(qo, qo, 4, True, n_xcd=1)
+    assert np.all(items[:, 1] > 0) and info["n_xcd"] == 1

@@ -1,0 +1,297 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Small cases are compared element by element on every row; the full-size
+workloads are compared on sampled rows the oracle computes one by one, plus
+properties that hold at any size. Inputs come from the seeded generators in
+`workloads`; the oracle reads host copies of the exact bytes the GPU used.
+"""
+import math
+import os
+
+import pytest
+import torch
+
+import mla_ragged_chunked_amd as mra
+import oracle
+import workloads
+from tests.parity import TOL, check, head_slice, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    mra.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _to(x: workloads.PrefillInputs, device):
+    return workloads.PrefillInputs(x.q.to(device), x.k.to(device), x.v.to(device), x.qo_indptr,
+                                   x.kv_indptr, x.num_heads, x.causal, x.sm_scale)
+
+
+def _full_parity(x: workloads.PrefillInputs, what):
+    """Run on the GPU and compare every row with the oracle."""
+    g = _to(x, DEV)
+    _flush(f"[gpu] {what}: T={x.qo_indptr[-1]} Tk={x.kv_indptr[-1]} H={x.num_heads} "
+           f"causal={x.causal} dtype={x.q.dtype}")
+    o, lse = mra.ragged_prefill(g.q, g.k, g.v, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale)
+    return check(o, lse, ro, rl, x.q.dtype, what)
+
+
+# ---------------------------------------------------------------------------
+# small workloads, every row
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_workload():
+    x = workloads.tiny_fp32()
+    _full_parity(x, "tiny fp32 {1,17,64} x 4 heads")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_tiny_workload_in_bf16(causal):
+    x = workloads.ragged_inputs([1, 17, 64], [1, 17, 64], 4, torch.bfloat16, seed=1,
+                                causal=causal)
+    _full_parity(x, f"tiny bf16 causal={causal}")
+
+
+TILE_EDGE_LENS = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_tile_edge_lengths(dtype, causal):
+    x = workloads.ragged_inputs(TILE_EDGE_LENS, TILE_EDGE_LENS, 3, dtype, seed=31, causal=causal)
+    _full_parity(x, f"tile edges dtype={dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_qo_kv_mismatch_and_empty_sequences(dtype, causal):
+    # qo > kv (causal rows with no key), kv = 0, qo = 0, kv > qo
+    qo_lens = [5, 300, 0, 7, 513, 1, 260]
+    kv_lens = [2, 0, 9, 40, 513, 700, 33]
+    x = workloads.ragged_inputs(qo_lens, kv_lens, 2, dtype, seed=32, causal=causal)
+    err = _full_parity(x, f"ragged mismatch dtype={dtype} causal={causal}")
+    _flush(f"    max errors O={err[0]:.2e} LSE={err[1]:.2e}")
+
+
+def test_single_visible_key_is_exact_in_bf16():
+    x = workloads.ragged_inputs([3, 300, 64], [3, 300, 64], 8, torch.bfloat16, seed=33)
+    g = _to(x, DEV)
+    o, lse = mra.ragged_prefill(g.q, g.k, g.v, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    torch.cuda.synchronize()
+    for b in range(x.batch):
+        t, j = x.qo_indptr[b], x.kv_indptr[b]
+        # one visible key: p = 1, l = 1, so O is that V row bit for bit
+        assert torch.equal(o[t].cpu(), x.v[j])
+        s = (x.q[t].double() * x.k[j].double()).sum(-1) * x.sm_scale
+        assert torch.allclose(lse[t].double().cpu(), s, atol=1e-5, rtol=0)
+
+
+def test_equal_keys_average_visible_values_on_gpu():
+    lens = [70, 300]
+    x = workloads.ragged_inputs(lens, lens, 2, torch.bfloat16, seed=34)
+    for b in range(x.batch):
+        a, e = x.kv_indptr[b], x.kv_indptr[b + 1]
+        x.k[a:e] = x.k[a:a + 1]
+    _full_parity(x, "equal keys")
+
+
+def test_more_heads_and_large_scores():
+    # a large scale makes the running max move a lot (the lazy rescale path)
+    lens = [400, 129]
+    x = workloads.ragged_inputs(lens, lens, 5, torch.bfloat16, seed=35, sm_scale=0.5)
+    _full_parity(x, "sm_scale 0.5")
+    x = workloads.ragged_inputs(lens, lens, 5, torch.bfloat16, seed=36, sm_scale=1e-3)
+    _full_parity(x, "sm_scale 1e-3")
+
+
+def test_plan_run_matches_one_shot_and_repeats():
+    lens = [300, 1, 129]
+    x = _to(workloads.ragged_inputs(lens, lens, 4, torch.bfloat16, seed=37), DEV)
+    o1, l1 = mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    for n_xcd in (8, 1):
+        p = mra.Plan(n_xcd=n_xcd).plan(x.qo_indptr, x.kv_indptr, 4, True).upload()
+        for _ in range(3):
+            o2, l2 = p.run(x.q, x.k, x.v, x.sm_scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # without LSE
+    o3 = mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, True, x.sm_scale,
+                            return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3)
+
+
+def test_one_shot_on_two_streams():
+    lens = [200, 90]
+    x = _to(workloads.ragged_inputs(lens, lens, 2, torch.bfloat16, seed=38), DEV)
+    ref, ref_l = mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for s in (s1, s2, s1, s2):
+        with torch.cuda.stream(s):
+            outs.append(mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, True,
+                                           x.sm_scale))
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o, ref) and torch.equal(l, ref_l)
+
+
+def test_native_library_is_loaded():
+    with open("/proc/self/maps") as fh:
+        maps = fh.read()
+    assert os.path.realpath(mra.LIB_PATH) in maps
+
+
+# ---------------------------------------------------------------------------
+# merge_state
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_merge_state_parity(dtype):
+    o_a, l_a, o_b, l_b = workloads.merge_inputs(3000, 8, dtype, seed=41, neg_inf_frac=0.2)
+    g = [t.to(DEV) for t in (o_a, l_a, o_b, l_b)]
+    o, l = mra.merge_state(*g)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(o_a, l_a, o_b, l_b)
+    check(o, l, ro, rl, dtype, f"merge {dtype}")
+
+
+def test_merge_state_in_place():
+    o_a, l_a, o_b, l_b = [t.to(DEV) for t in
+                          workloads.merge_inputs(777, 4, torch.bfloat16, seed=42, neg_inf_frac=0.1)]
+    ref_o, ref_l = mra.merge_state(o_a, l_a, o_b, l_b)
+    mra.merge_state(o_a, l_a, o_b, l_b, out=o_a, out_lse=l_a)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, ref_o) and torch.equal(l_a, ref_l)
+
+
+# ---------------------------------------------------------------------------
+# decompression
+# ---------------------------------------------------------------------------
+
+def test_decompress_small_parity():
+    d = workloads.decompress_batch(num_seqs=2, seq_len=300, num_heads=3)
+    k, v = mra.decompress_kv(d.c_kv.to(DEV), d.k_rope.to(DEV), d.w_uk.to(DEV), d.w_uv.to(DEV), 3)
+    torch.cuda.synchronize()
+    rk, rv = oracle.decompress(d.c_kv, d.k_rope, d.w_uk, d.w_uv, 3)
+    k, v = k.double().cpu(), v.double().cpu()
+    # k_rope is copied, not computed
+    assert torch.equal(k[:, :, 128:], rk[:, :, 128:])
+    # bf16 output rounding (half an ulp, 2^-9 relative) plus fp32 accumulation
+    for got, want in ((k[:, :, :128], rk[:, :, :128]), (v, rv)):
+        err = (got - want).abs()
+        assert torch.all(err <= want.abs() * 2.0 ** -8 + 1e-4), err.max()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# ---------------------------------------------------------------------------
+
+def _sampled_parity(g: workloads.PrefillInputs, o, lse, heads, rows, what, q_host=None,
+                    k_host=None, v_host=None):
+    """Compare sampled rows of heads `heads` with the oracle (per-head host copies)."""
+    for h in heads:
+        qh = head_slice(g.q, h) if q_host is None else q_host(h)
+        kh = head_slice(g.k, h) if k_host is None else k_host(h)
+        vh = head_slice(g.v, h) if v_host is None else v_host(h)
+        ro, rl = oracle.prefill(qh, kh, vh, g.qo_indptr, g.kv_indptr, g.causal, g.sm_scale,
+                                rows)
+        idx = torch.tensor(rows)
+        check(o[idx, h:h + 1].cpu(), lse[idx, h:h + 1].cpu(), ro, rl,
+              g.q.dtype if q_host is None else torch.bfloat16, f"{what} head {h}")
+
+
+def _row_properties(o, lse):
+    assert torch.isfinite(o).all(), "non-finite O"
+    assert torch.isfinite(lse).all(), "non-finite LSE (every row sees a key here)"
+
+
+def test_deepseek_v3_batch_full_size():
+    g = workloads.deepseek_v3_batch(device=DEV)
+    _flush(f"[gpu] deepseek_v3_batch T={g.qo_indptr[-1]} lens={g.qo_indptr}")
+    o, lse = mra.ragged_prefill(g.q, g.k, g.v, g.qo_indptr, g.kv_indptr, True, g.sm_scale)
+    torch.cuda.synchronize()
+    _row_properties(o, lse)
+    rows = sample_rows(g.qo_indptr, n_random=128, seed=2)
+    _sampled_parity(g, o, lse, [0, 77, 127], rows, "deepseek_v3_batch")
+
+
+def test_chunked_prefill_full_size():
+    c = workloads.chunked_prefill(device=DEV)
+    m = c.main
+    _flush(f"[gpu] chunked_prefill: {len(c.chunks)} context chunks")
+    parts = [mra.ragged_prefill(ch.q, ch.k, ch.v, ch.qo_indptr, ch.kv_indptr, False, ch.sm_scale)
+             for ch in c.chunks]
+    parts.append(mra.ragged_prefill(m.q, m.k, m.v, m.qo_indptr, m.kv_indptr, True, m.sm_scale))
+    o, lse = parts[0]
+    for o2, l2 in parts[1:]:
+        o, lse = mra.merge_state(o, lse, o2, l2)
+    torch.cuda.synchronize()
+    _row_properties(o, lse)
+    rows = sample_rows(m.qo_indptr, n_random=64, seed=3)
+    idx = torch.tensor(rows)
+    for h in (0, 101):
+        q = head_slice(m.q, h)
+        chunk_kvs = [(head_slice(ch.k, h), head_slice(ch.v, h), ch.kv_indptr) for ch in c.chunks]
+        ro, rl, rparts = oracle.chunked(q, head_slice(m.k, h), head_slice(m.v, h), m.qo_indptr,
+                                        chunk_kvs, m.sm_scale, rows)
+        for (po, pl), (qo_, ql_) in zip(parts, rparts):
+            check(po[idx, h:h + 1].cpu(), pl[idx, h:h + 1].cpu(), qo_, ql_, torch.bfloat16,
+                  f"chunked partial head {h}")
+        check(o[idx, h:h + 1].cpu(), lse[idx, h:h + 1].cpu(), ro, rl, torch.bfloat16,
+              f"chunked merged head {h}")
+
+
+def test_skewed_batch_full_size():
+    g = workloads.skewed_batch(device=DEV)
+    _flush(f"[gpu] skewed_batch T={g.qo_indptr[-1]} max_len="
+           f"{max(b - a for a, b in zip(g.qo_indptr, g.qo_indptr[1:]))}")
+    o, lse = mra.ragged_prefill(g.q, g.k, g.v, g.qo_indptr, g.kv_indptr, True, g.sm_scale)
+    torch.cuda.synchronize()
+    _row_properties(o, lse)
+    rows = sample_rows(g.qo_indptr, n_random=64, seed=4)
+    rows = rows[::3]   # keep the oracle to seconds
+    _sampled_parity(g, o, lse, [5], rows, "skewed_batch")
+    del g, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_decompress_then_prefill_full_size():
+    d = workloads.decompress_batch(device=DEV)
+    H = d.num_heads
+    _flush(f"[gpu] decompress_batch T={d.indptr[-1]} H={H}")
+    k, v = mra.decompress_kv(d.c_kv, d.k_rope, d.w_uk, d.w_uv, H)
+    o, lse = mra.ragged_prefill(d.q, k, v, d.indptr, d.indptr, True, d.sm_scale)
+    torch.cuda.synchronize()
+    _row_properties(o, lse)
+    c_kv, k_rope = d.c_kv.cpu(), d.k_rope.cpu()
+    rows = sample_rows(d.indptr, n_random=32, seed=5)
+    idx = torch.tensor(rows)
+    for h in (3,):
+        wk = d.w_uk[:, h * 128:(h + 1) * 128].contiguous().cpu()
+        wv = d.w_uv[:, h * 128:(h + 1) * 128].contiguous().cpu()
+        rk, rv = oracle.decompress(c_kv, k_rope, wk, wv, 1)           # fp64, all tokens
+        # decompressed K/V for this head, sampled tokens: bf16 rounding bound
+        gk = k[idx, h:h + 1].double().cpu()
+        gv = v[idx, h:h + 1].double().cpu()
+        assert torch.all((gk - rk[idx]).abs() <= rk[idx].abs() * 2.0 ** -8 + 1e-4)
+        assert torch.all((gv - rv[idx]).abs() <= rv[idx].abs() * 2.0 ** -8 + 1e-4)
+        qh = head_slice(d.q, h).double()
+        ro, rl = oracle.prefill(qh, rk, rv, d.indptr, d.indptr, True, d.sm_scale, rows)
+        check(o[idx, h:h + 1].cpu(), lse[idx, h:h + 1].cpu(), ro, rl, torch.bfloat16,
+              f"decompress+prefill head {h}")
