@@ -56,6 +56,35 @@ def visible_pairs(qo, kv, causal):
     return n
 
 
+def code_hash(path):
+    """sha256 (16 hex) of a source file's code with comments and blank lines removed."""
+    import hashlib
+    import re
+    txt = open(path).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    lines = [l.split("//")[0].strip() for l in txt.splitlines()]
+    return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()[:16]
+
+
+def profile_traffic(profile, source):
+    """HBM bytes per launch from a committed counter profile, or None when the
+    profile is missing or the kernel's code changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("source_code_sha256_16") != code_hash(os.path.join(ROOT, source)):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -65,6 +94,9 @@ def parse():
                     help="target CPU time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit; "
+                         "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
     return ap.parse_args()
 
 
@@ -166,8 +198,17 @@ def main():
     import mla_ragged_chunked_amd as mra
     import workloads
 
-    mra.lib()
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times (read {n} B + write {n} B per copy)")
+        return
+    mra.lib()
     t0 = time.perf_counter()
     x = workloads.deepseek_v3_batch(device="cuda")
     torch.cuda.synchronize()
@@ -205,7 +246,9 @@ def main():
                    "n_xcd": info["n_xcd"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_bf16_kernel",
+                     "traffic": profile_traffic("prefill_bf16_deepseek_v3_batch.txt",
+                                                "mla_ragged_chunked_amd/csrc/prefill_bf16.hip"),
+                     "kernel": "prefill_bf16_kernel",
                      "kernel_ms": round(k_ms, 4)},
     }
     if not args.no_secondary:

@@ -174,7 +174,7 @@ int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, in
     if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
     if (heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
     if (batch > 0 && (qo == nullptr || kv == nullptr)) return fail(MLA_EINVAL, "indptr is NULL");
-    const int bm = dtype == MLA_DTYPE_BF16 ? mla::kBf16BlockM : mla::kFp32BlockM;
+    const int bm = dtype == MLA_DTYPE_BF16 ? mla::prefill_bf16_block_m() : mla::prefill_fp32_block_m();
     std::string err;
     try {
         if (!mla::build_work_list(qo, kv, batch, heads, causal != 0, bm, p->n_xcd, p->items, err))

@@ -31,9 +31,10 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
 
-// Query-tile heights of the two prefill kernels.
-constexpr int kBf16BlockM = 256;   // 4 waves x 64 rows
-constexpr int kFp32BlockM = 64;    // 1 wave  x 64 rows
+// Query-tile heights of the two prefill kernels (each kernel file owns its
+// tile shape; the planner asks for it).
+int prefill_bf16_block_m();
+int prefill_fp32_block_m();
 
 // Build the ordered work list (host only). Returns false with `err` set on
 // invalid input. `block_m` is the query-tile height, `n_xcd` the number of

@@ -9,33 +9,48 @@
 // manage kv_cache?" (192 for query/key, 128 for value/output).
 //
 // Design (MI355X):
-//  * One workgroup = 4 waves x 64 query rows. Each wave keeps its 64 Q rows
-//    in VGPRs as MFMA B operands for the whole item (96 VGPRs).
+//  * One workgroup = 4 waves x 32 query rows (128-row tiles); two workgroups
+//    share a CU (2 waves per SIMD, about 230 VGPRs, no AGPRs, 80 KB LDS
+//    each), so one wave's VALU work also overlaps the other wave's MFMAs.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from LDS, B = 16 dims x
-//    32 queries. In the accumulator each lane then owns one query column and
-//    16 keys, so row max / row sum are in-lane plus one exchange between the
-//    two 32-lane halves.
-//  * The same accumulator, rounded to bf16, is directly the B operand of
-//    O^T = V^T P^T, provided V^T's key columns in LDS are permuted to match
-//    the accumulator's row order: accumulator slot (i, half g) of a 32-key
-//    block holds key 8*(i/4) + 4*g + (i%4); the PV k-slot 8*g + e of MFMA m
-//    must hold key 16*m + 8*(e/4) + 4*g + (e%4). Storing key j at LDS column
-//    sigma(j) = j with bits 2 and 3 swapped makes every A fragment one
-//    contiguous 16-byte read.
-//  * K (row-major, 400-byte pitch) and V^T (key-permuted, 80-byte pitch)
-//    tiles of 32 keys are staged in LDS with two stages: tile t+1 is fetched
-//    into VGPRs while tile t is computed, then written to the other stage;
-//    one barrier per tile. Pitches are padded so fragment reads of
-//    consecutive rows fall in distinct banks.
-//  * Online softmax in base 2 with sm_scale * log2(e) folded into one FMA;
-//    the running max is only raised when it grows by more than 2^8 (the
-//    stale max keeps every p <= 256, exact after the final division), so the
-//    O rescale is skipped on most tiles. The row sum is accumulated from the
-//    bf16-rounded p that enter the MFMA, so O is normalised by exactly the
-//    weights it was built from.
-//  * Keys past the sequence end are zero-filled (no NaN can reach the PV
-//    product); rows with no visible key get O = 0, LSE = -inf.
+//    32 queries (Q stays in VGPRs for the whole item). In the accumulator
+//    each lane owns one query column and 16 keys, so row max / row sum are
+//    in-lane plus one v_permlane32_swap between the two 32-lane halves.
+//  * That accumulator, rounded to bf16, is directly the B operand of
+//    O^T = V^T P^T. Accumulator slot (i, half g) of a 32-key block holds key
+//    8*(i/4) + 4*g + (i%4), so the V^T A operand for PV MFMA m needs, in
+//    k-slot 8*g + e, key 16*m + 8*(e/4) + 4*g + (e%4). V is kept row-major in
+//    LDS and read with ds_read_b64_tr_b16 (within each 16-lane group, lane
+//    4r+q supplies 4 values of row r and lane j receives column j), each lane
+//    addressing the key rows that slot order requires.
+//  * K/V tiles of 32 keys are loaded straight from HBM into a 4-stage LDS
+//    ring with global_load_lds_dwordx4 (no VGPR staging). K is stored in
+//    1 KB blocks of 8 rows x 128 contiguous bytes (8 cache lines per load
+//    instruction) with the 16-byte chunks of each row XOR-swizzled so the
+//    MFMA fragment reads are bank-conflict free; V rows are 256 B with an XOR
+//    swizzle of their chunks for the transposing reads. Addresses are a
+//    per-tile scalar base plus a per-lane 32-bit offset computed once per
+//    item (recomputed with a clamp only on a sequence's last tile).
+//  * Software pipeline, one barrier per tile: iteration j publishes tile j+1
+//    (and retires tile j-1), puts tile j+3 in flight into tile j-1's stage,
+//    computes the scores of tile j+1 and runs softmax + PV of tile j, so
+//    every wave always has independent MFMA and VALU work to interleave.
+//  * Online softmax in base 2 with sm_scale * log2(e) folded into one FMA.
+//    The running max is raised only when a tile's max exceeds it by more
+//    than 2^8 (a stale max keeps every p <= 256 and is exact after the final
+//    division), so the O rescale is a rarely taken wave-uniform branch (at
+//    least once per item, since the max starts at -inf).
+//  * Tiles run in three wave-uniform phases: tiles every row of the wave sees
+//    in full (no mask code), diagonal / ragged-edge tiles (masked), then
+//    tiles only other waves need (loads and barrier only).
+//  * The row sum is accumulated from the bf16-rounded p that enter the MFMA
+//    (v_dot2 with (1, 1)), so O is normalised by exactly the weights it was
+//    built from.
+//  * Keys past the sequence end load the last valid row (finite data) and
+//    are masked to p = 0; rows with no visible key get O = 0, LSE = -inf.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace mla {
@@ -44,278 +59,335 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 64;
-constexpr int kBM = kWaves * kRowsPerWave;
-static_assert(kBM == kBf16BlockM, "tile height must match the planner");
+constexpr int kBM = kWaves * 32;                    // 32 query rows per wave
 constexpr int kBN = 32;                             // keys per KV tile
-constexpr int kKSteps = kDqk / 16;                  // 12 MFMA k-steps over 192 dims
-constexpr int kKPitch = kDqk * 2 + 16;              // bytes per K row in LDS
-constexpr int kVPitch = kBN * 2 + 16;               // bytes per V^T row in LDS
-constexpr int kKBytes = kBN * kKPitch;
-constexpr int kVBytes = kDvo * kVPitch;
-constexpr int kStage = kKBytes + kVBytes;
-constexpr int kKChunks = kBN * (kDqk / 8);          // 16-byte chunks per K tile
-constexpr int kKPerThread = kKChunks / kThreads;
-constexpr int kVUnits = (kBN / 2) * (kDvo / 8);     // (key pair, 16-byte chunk) units
-constexpr int kVPerThread = kVUnits / kThreads;
-static_assert(kKChunks % kThreads == 0 && kVUnits % kThreads == 0, "staging split");
-constexpr float kLazyRescale = 8.0f;                // log2 units
+constexpr int kKSteps = kDqk / 16;                  // 12
+constexpr int kKBytes = kBN * kDqk * 2;             // 12 KB: 12 fragment blocks of 1 KB
+constexpr int kVBytes = kBN * kDvo * 2;             // 8 KB: 8 blocks of 4 rows x 256 B
+constexpr int kStage = kKBytes + kVBytes;           // 20 KB
+constexpr int kStages = 4;
+constexpr int kKBlocksPerWave = (kKBytes / 1024) / kWaves;   // 3
+constexpr int kVBlocksPerWave = (kVBytes / 1024) / kWaves;   // 2
+constexpr int kLoadsPerTile = kKBlocksPerWave + kVBlocksPerWave;
+constexpr float kLazyRescale = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ int sigma(int j) {
-    return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ int lim_of(int r, int diag0, int kv_len) {
     int n = diag0 + r + 1;
     n = n < 0 ? 0 : n;
     return n > kv_len ? kv_len : n;
 }
+// 16-byte chunk slot of chunk c in V row `row` (XOR swizzle over 4-chunk groups)
+__device__ __forceinline__ int vslot(int row, int c) { return c ^ ((row & 3) << 2); }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes land at
+// lds_base + 16 * l. Issued as inline asm so the compiler does not see LDS
+// DMA in flight (it would wait for all of it before every LDS read); the
+// kernel waits for completion itself with wait_vmcnt before the barrier
+// that publishes a tile. Nothing else in this kernel uses M0.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds_dst) {
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    // readfirstlane returns int: take each half as uint32_t before widening,
+    // or a low word with bit 31 set would sign-extend into the high word
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
                          const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                          uint16_t* __restrict__ out, float* __restrict__ lse, int num_heads,
                          float scale_log2) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
     const WorkItem it = items[blockIdx.x];
     if (it.n_rows <= 0) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int H = num_heads;
-    const int row_w0 = wave * kRowsPerWave;
+    const int row_w0 = wave * 32;
     int wave_rows = it.n_rows - row_w0;
-    wave_rows = wave_rows < 0 ? 0 : (wave_rows > kRowsPerWave ? kRowsPerWave : wave_rows);
-    const bool wave_active = wave_rows > 0;
-    const int wave_lo = wave_active ? lim_of(row_w0, it.diag0, it.kv_len) : 0;
-    const int wave_hi = wave_active ? lim_of(row_w0 + wave_rows - 1, it.diag0, it.kv_len) : 0;
+    wave_rows = wave_rows < 0 ? 0 : (wave_rows > 32 ? 32 : wave_rows);
+    const int wave_lo = wave_rows > 0 ? lim_of(row_w0, it.diag0, it.kv_len) : 0;
+    const int wave_hi = wave_rows > 0 ? lim_of(row_w0 + wave_rows - 1, it.diag0, it.kv_len) : 0;
 
-    // ---- Q fragments: rows row_w0 + 32*qb + l32, dims 16*s + 8*g .. +8
-    bf16x8_t qf[2][kKSteps];
-    int my_lim[2];
+    // Q fragments (B operand): row row_w0 + l32, dims 16*s + 8*g .. +8
+    bf16x8_t qf[kKSteps];
+    const int my_row = row_w0 + l32;
+    const int my_lim = lim_of(my_row, it.diag0, it.kv_len);
+    if (my_row < it.n_rows) {
+        const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(
+            q + ((int64_t)(it.q_row0 + my_row) * H + it.head) * kDqk);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = row_w0 + qb * 32 + l32;
-        my_lim[qb] = lim_of(r, it.diag0, it.kv_len);
-        if (r < it.n_rows) {
-            const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(
-                q + ((int64_t)(it.q_row0 + r) * H + it.head) * kDqk);
+        for (int s = 0; s < kKSteps; ++s) qf[s] = src[s * 2 + g];
+    } else {
 #pragma unroll
-            for (int s = 0; s < kKSteps; ++s) qf[qb][s] = src[s * 2 + g];
-        } else {
-#pragma unroll
-            for (int s = 0; s < kKSteps; ++s) qf[qb][s] = bf16x8_t{};
-        }
+        for (int s = 0; s < kKSteps; ++s) qf[s] = bf16x8_t{};
     }
 
-    f32x16_t oacc[4][2];
+    f32x16_t oacc[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x16_t{};
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // ---- K/V staging through VGPRs
-    u32x4_t kreg[kKPerThread];
-    u32x4_t vreg[kVPerThread][2];
-    const int64_t kv_row_base = (int64_t)it.kv_start * H + it.head;
-
-    auto load_tile = [&](int key0) {
+    // ---- direct global -> LDS staging ----
+    // K: 12 blocks of 1 KB per tile; block 3R + G holds rows 8R .. 8R+7, each
+    // row's 16-byte chunks 8G .. 8G+7 at slot (chunk ^ (row/2)) % 8.
+    // V: 8 blocks of 4 rows x 256 B; row r's chunk c sits at slot vslot(r, c).
+    // Keys at or past kv_len load the last valid row instead (finite data;
+    // the mask gives those keys p = 0).
+    const int64_t kv_row0 = (int64_t)it.kv_start * H + it.head;   // row index of key 0
+    const int last_key = it.kv_len - 1;
+    // Per-lane byte offsets (from the tile's first key row) of this wave's
+    // loads: 3 K blocks and 2 V blocks; recomputed with the clamp only on a
+    // sequence's last tile.
+    const uint32_t krow = (uint32_t)H * kDqk * 2;
+    const uint32_t vrow = (uint32_t)H * kDvo * 2;
+    int ld_row[kKBlocksPerWave + kVBlocksPerWave];
+    uint32_t ld_col[kKBlocksPerWave + kVBlocksPerWave];
 #pragma unroll
-        for (int j = 0; j < kKPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int row = u / (kDqk / 8);
-            const int c = u % (kDqk / 8);
-            const int key = key0 + row;
-            if (key < it.kv_len) {
-                kreg[j] = *reinterpret_cast<const u32x4_t*>(
-                    k + (kv_row_base + (int64_t)key * H) * kDqk + c * 8);
-            } else {
-                kreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int j = 0; j < kKBlocksPerWave; ++j) {
+        // block bi = 3 R + G: rows 8R .. 8R+7, 16-byte chunks 8G .. 8G+7 of
+        // each row (128 contiguous bytes per row), chunk order XOR-swizzled
+        const int bi = wave * kKBlocksPerWave + j;
+        ld_row[j] = (bi / 3) * 8 + (lane >> 3);
+        ld_col[j] = ((bi % 3) * 8 + ((lane & 7) ^ ((ld_row[j] >> 1) & 7))) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kVBlocksPerWave; ++j) {
+        const int b = wave * kVBlocksPerWave + j;
+        ld_row[kKBlocksPerWave + j] = 4 * b + (lane >> 4);
+        ld_col[kKBlocksPerWave + j] = vslot(ld_row[kKBlocksPerWave + j], lane & 15) * 16;
+    }
+    uint32_t ld_off[kKBlocksPerWave + kVBlocksPerWave];
+#pragma unroll
+    for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j)
+        ld_off[j] = (uint32_t)ld_row[j] * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
+    const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k + kv_row0 * kDqk);
+    const uint8_t* vseq = reinterpret_cast<const uint8_t*>(v + kv_row0 * kDvo);
+    auto issue_tile = [&](int kt, int stage) {
+        uint8_t* ks = smem + stage * kStage;
+        uint8_t* vs = ks + kKBytes;
+        const int key0 = kt * kBN;
+        const uint8_t* kb = kseq + (uint64_t)key0 * krow;
+        const uint8_t* vb = vseq + (uint64_t)key0 * vrow;
+        uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
+        if (key0 + kBN - 1 > last_key) {
+            const int lim = last_key - key0;
+#pragma unroll
+            for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j) {
+                const int r = ld_row[j] < lim ? ld_row[j] : lim;
+                off[j] = (uint32_t)r * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j) off[j] = ld_off[j];
         }
 #pragma unroll
-        for (int j = 0; j < kVPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int p = u % (kBN / 2);
-            const int c = u / (kBN / 2);
+        for (int j = 0; j < kKBlocksPerWave; ++j)
+            dma16(kb, off[j], ks + (wave * kKBlocksPerWave + j) * 1024);
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int key = key0 + 2 * p + h2;
-                if (key < it.kv_len) {
-                    vreg[j][h2] = *reinterpret_cast<const u32x4_t*>(
-                        v + (kv_row_base + (int64_t)key * H) * kDvo + c * 8);
-                } else {
-                    vreg[j][h2] = u32x4_t{0u, 0u, 0u, 0u};
-                }
+        for (int j = 0; j < kVBlocksPerWave; ++j)
+            dma16(vb, off[kKBlocksPerWave + j], vs + (wave * kVBlocksPerWave + j) * 1024);
+    };
+
+    // LDS offsets of this lane's K fragment (row l32, chunk 2s + g) for
+    // k-steps s = 4u + t: block 3 (l32/8) + u, slot 8 (l32%8) + ((2t+g) ^ ((l32/2)%8))
+    int k_off[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        k_off[t] = (l32 >> 3) * 3 * 1024 + ((l32 & 7) * 8 + ((2 * t + g) ^ ((l32 >> 1) & 7))) * 16;
+
+    // ---- compute pieces ----
+    auto scores = [&](int kt, int stage, auto masked, f32x16_t& sacc) {
+        constexpr bool kMasked = decltype(masked)::value;
+        const uint8_t* ks = smem + stage * kStage;
+        sacc = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + k_off[s & 3] + (s >> 2) * 1024);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
+        }
+        if constexpr (kMasked) {
+            const int key0 = kt * kBN;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + (i >> 2) * 8 + g * 4 + (i & 3);
+                sacc[i] = key < my_lim ? sacc[i] : -INFINITY;
             }
         }
     };
-
-    auto store_tile = [&](int stage) {
-        uint8_t* ks = smem + stage * kStage;
-        uint8_t* vs = ks + kKBytes;
+    auto tile_max = [&](const f32x16_t& sv) {
+        float mx = sv[0];
 #pragma unroll
-        for (int j = 0; j < kKPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int row = u / (kDqk / 8);
-            const int c = u % (kDqk / 8);
-            *reinterpret_cast<u32x4_t*>(ks + row * kKPitch + c * 16) = kreg[j];
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+        return xor32_max(mx) * scale_log2;
+    };
+    // V^T fragment for dv block db, key step mm (16 keys): two transposing
+    // reads of 4 keys each. Lane (g, h = bit 4, j = low 4 bits, r = j/4,
+    // q = j%4) supplies row mm*16 + t*8 + g*4 + r, dims db*32 + h*16 + 4q.
+    const int tr_h = (lane >> 4) & 1;
+    const int tr_r = (lane & 15) >> 2;
+    const int tr_q = lane & 3;
+    auto vfrag = [&](const uint8_t* vs, int db, int mm) {
+        bf16x8_t a;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = mm * 16 + t * 8 + g * 4 + tr_r;
+            const int chunk = db * 4 + tr_h * 2 + (tr_q >> 1);
+            const uint8_t* p = vs + row * 256 + vslot(row, chunk) * 16 + (tr_q & 1) * 8;
+            const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+            const bf16x4_t y = __builtin_bit_cast(bf16x4_t, x);
+            a[t * 4 + 0] = y[0];
+            a[t * 4 + 1] = y[1];
+            a[t * 4 + 2] = y[2];
+            a[t * 4 + 3] = y[3];
         }
+        return a;
+    };
+    auto accumulate = [&](int stage, const f32x16_t& sacc) {
+        const uint8_t* vs = smem + stage * kStage + kKBytes;
+        bf16x8_t pf[2];
+        const float msub = m_run == -INFINITY ? 0.0f : m_run;
+        float lsum = l_run;
 #pragma unroll
-        for (int j = 0; j < kVPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int p = u % (kBN / 2);
-            const int c = u / (kBN / 2);
-            const int col = sigma(2 * p);    // sigma(2p + 1) == sigma(2p) + 1
+        for (int mm = 0; mm < 2; ++mm) {
+            bf16x8_t frag;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w0 = vreg[j][0][e >> 1];
-                const uint32_t w1 = vreg[j][1][e >> 1];
-                const uint32_t packed = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                                : ((w0 & 0xffffu) | (w1 << 16));
-                *reinterpret_cast<uint32_t*>(vs + (c * 8 + e) * kVPitch + col * 2) = packed;
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mm * 8 + e], scale_log2, -msub));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mm * 8 + e + 1], scale_log2, -msub));
+                const bf16x2_t pk = {(__bf16)p0, (__bf16)p1};
+                frag[e] = pk[0];
+                frag[e + 1] = pk[1];
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes, lsum, false);
+            }
+            pf[mm] = frag;
+        }
+        l_run = lsum;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                const bf16x8_t a = vfrag(vs, db, mm);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[mm], oacc[db], 0, 0, 0);
             }
         }
     };
 
     const int n_tiles = (it.kv_hi + kBN - 1) / kBN;
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
+    const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
+    const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
+
+    // Software pipeline: iteration j computes the scores of tile j+1 (K of
+    // stage (j+1)%4) while it runs the softmax and PV of tile j (V of stage
+    // j%4), so each wave always has independent MFMA and VALU work. Loads run
+    // two tiles ahead of the K use.
+    //   top of iteration j: wait for this wave's loads of tile j+1, barrier
+    //   (publishes tile j+1 and retires tile j-1), put tile j+3 in flight
+    //   into tile j-1's stage.
+    auto sync_top = [&](int j) {
+        // loads issued so far: tiles 0 .. j+2; tile j+1 must be complete
+        if (j + 2 < n_tiles) wait_vmcnt<kLoadsPerTile>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (j + 3 < n_tiles) issue_tile(j + 3, (j + 3) % kStages);
+    };
+
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+        if (t < n_tiles) issue_tile(t, t);
+    // tile 0 must be complete: tiles 1 and 2 may still be in flight
+    if (n_tiles > 2) wait_vmcnt<2 * kLoadsPerTile>();
+    else if (n_tiles > 1) wait_vmcnt<kLoadsPerTile>();
+    else wait_vmcnt<0>();
     __syncthreads();
 
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        const int key0 = kt * kBN;
-        const bool has_next = kt + 1 < n_tiles;
-        if (has_next) load_tile(key0 + kBN);
-
-        if (wave_active && key0 < wave_hi) {
-            const uint8_t* ks = smem + (kt & 1) * kStage;
-            const uint8_t* vs = ks + kKBytes;
-
-            // S^T = K Q^T for 32 keys x 64 queries
-            f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-            for (int s = 0; s < kKSteps; ++s) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                    ks + l32 * kKPitch + (s * 16 + g * 8) * 2);
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][s], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][s], sacc[1], 0, 0, 0);
-            }
-
-            const bool need_mask = key0 + kBN > wave_lo;
-            bf16x8_t pf[2][2];
-            bool any_rescale = false;
-            float alpha[2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                if (need_mask) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + (i >> 2) * 8 + g * 4 + (i & 3);
-                        if (key >= my_lim[qb]) sacc[qb][i] = -INFINITY;
-                    }
-                }
-                float mx = sacc[qb][0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qb][i]);
-                mx = fmaxf(mx, xor32(mx));
-                const float m_tile = mx * scale_log2;    // -inf stays -inf (scale > 0)
-                const float m_old = m_run[qb];
-                const bool raise = m_tile > m_old + kLazyRescale;
-                const float m_new = raise ? m_tile : m_old;
-                alpha[qb] = raise ? __builtin_amdgcn_exp2f(m_old - m_new) : 1.0f;
-                any_rescale |= raise;
-                m_run[qb] = m_new;
-                const float msub = m_new == -INFINITY ? 0.0f : m_new;
-
-                float lsum = 0.f;
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    bf16x8_t frag;
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const float p0 = __builtin_amdgcn_exp2f(
-                            __builtin_fmaf(sacc[qb][mm * 8 + e], scale_log2, -msub));
-                        const float p1 = __builtin_amdgcn_exp2f(
-                            __builtin_fmaf(sacc[qb][mm * 8 + e + 1], scale_log2, -msub));
-                        const bf16x2_t pk = {(__bf16)p0, (__bf16)p1};
-                        frag[e] = pk[0];
-                        frag[e + 1] = pk[1];
-                        lsum += (float)pk[0] + (float)pk[1];
-                    }
-                    pf[qb][mm] = frag;
-                }
-                l_run[qb] = l_run[qb] * alpha[qb] + lsum;
-            }
-
-            // wave-uniform: rescale O only when some row raised its max
-            if (__any(any_rescale)) {
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) oacc[db][qb] *= alpha[qb];
-            }
-
-            // O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                        vs + (db * 32 + l32) * kVPitch + (mm * 16 + g * 8) * 2);
-                    oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0][mm], oacc[db][0], 0, 0, 0);
-                    oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1][mm], oacc[db][1], 0, 0, 0);
-                }
-            }
-        }
-
-        if (has_next) store_tile((kt + 1) & 1);
-        __syncthreads();
+    f32x16_t s_cur;
+    if (n_wave > 0) {
+        if (n_full > 0) scores(0, 0, std::false_type{}, s_cur);
+        else scores(0, 0, std::true_type{}, s_cur);
     }
-
-    // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-    if (!wave_active) return;
+    // one pipelined iteration; kNext: 0 = no next tile, 1 = unmasked, 2 = masked
+    auto iteration = [&](int j, auto next_kind) {
+        constexpr int kNext = decltype(next_kind)::value;
+        sync_top(j);
+        const float mt = tile_max(s_cur);
+        if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = row_w0 + qb * 32 + l32;
-        const float ltot = l_run[qb] + xor32(l_run[qb]);
-        if (r >= it.n_rows) continue;
-        const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
-        const int64_t orow = (int64_t)(it.q_row0 + r) * H + it.head;
-        uint16_t* dst = out + orow * kDvo;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const int dv = db * 32 + grp * 8 + g * 4;
-                bf16x4_t o4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][qb][grp * 4 + e] * inv);
-                *reinterpret_cast<bf16x4_t*>(dst + dv) = o4;
-            }
+            for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         }
-        if (g == 0 && lse != nullptr)
-            lse[orow] = ltot > 0.f ? (m_run[qb] + __log2f(ltot)) * kLn2 : -INFINITY;
+        f32x16_t s_next;
+        if constexpr (kNext == 1) scores(j + 1, (j + 1) % kStages, std::false_type{}, s_next);
+        if constexpr (kNext == 2) scores(j + 1, (j + 1) % kStages, std::true_type{}, s_next);
+        accumulate(j % kStages, s_cur);
+        if constexpr (kNext != 0) s_cur = s_next;
+    };
+    int j = 0;
+    for (; j + 1 < n_full; ++j) iteration(j, std::integral_constant<int, 1>{});
+    for (; j + 1 < n_wave; ++j) iteration(j, std::integral_constant<int, 2>{});
+    if (j < n_wave) { iteration(j, std::integral_constant<int, 0>{}); ++j; }
+    for (; j < n_tiles; ++j) sync_top(j);
+    wait_vmcnt<0>();
+
+    // ---- epilogue
+    if (wave_rows <= 0) return;
+    const float ltot = xor32_sum(l_run);
+    if (my_row >= it.n_rows) return;
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
+    const int64_t orow = (int64_t)(it.q_row0 + my_row) * H + it.head;
+    uint16_t* dst = out + orow * kDvo;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            const int dv = db * 32 + grp * 8 + g * 4;
+            bf16x4_t o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][grp * 4 + e] * inv);
+            *reinterpret_cast<bf16x4_t*>(dst + dv) = o4;
+        }
     }
+    if (g == 0 && lse != nullptr)
+        lse[orow] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
+
+int prefill_bf16_block_m() { return kBM; }
 
 hipError_t launch_prefill_bf16(const WorkItem* items, int64_t n_items, const void* q,
                                const void* k, const void* v, void* out, float* lse,

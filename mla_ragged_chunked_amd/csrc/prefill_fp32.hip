@@ -19,7 +19,6 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 64;
-static_assert(kThreads == kFp32BlockM, "tile height must match the planner");
 constexpr int kBN = 32;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -107,6 +106,8 @@ __global__ __launch_bounds__(kThreads) void prefill_fp32_kernel(
 }
 
 }  // namespace
+
+int prefill_fp32_block_m() { return kThreads; }
 
 hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const void* q,
                                const void* k, const void* v, void* out, float* lse,
