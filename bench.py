@@ -94,6 +94,8 @@ def parse():
                     help="target CPU time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
+    ap.add_argument("--only", choices=["merge"], default=None,
+                    help="run only one secondary kernel (for profiling) and print its figures")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; "
                          "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
@@ -188,6 +190,86 @@ def time_merge(mra, torch, workloads, steps, warmup):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 
 
+def time_chunked(mra, torch, workloads, steps, warmup):
+    """Chunked prefill pipeline: one causal pass over the new tokens, one
+    non-causal pass per context chunk, then merge_state folds the partials."""
+    c = workloads.chunked_prefill(device="cuda")
+    m = c.main
+    plans = [mra.Plan().plan(ch.qo_indptr, ch.kv_indptr, ch.num_heads, False).upload()
+             for ch in c.chunks]
+    plans.append(mra.Plan().plan(m.qo_indptr, m.kv_indptr, m.num_heads, True).upload())
+    passes = [(p, ch) for p, ch in zip(plans, c.chunks + [m])]
+    outs = [(torch.empty((m.q.shape[0], m.num_heads, 128), dtype=m.q.dtype, device="cuda"),
+             torch.empty((m.q.shape[0], m.num_heads), dtype=torch.float32, device="cuda"))
+            for _ in passes]
+    fo, fl = torch.empty_like(outs[0][0]), torch.empty_like(outs[0][1])
+
+    def step():
+        for (p, x), (o, l) in zip(passes, outs):
+            p.run(x.q, x.k, x.v, x.sm_scale, out=o, lse=l)
+        mra.merge_state(outs[0][0], outs[0][1], outs[1][0], outs[1][1], out=fo, out_lse=fl)
+        mra.merge_state(fo, fl, outs[2][0], outs[2][1], out=fo, out_lse=fl)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    pairs = sum(visible_pairs(x.qo_indptr, x.kv_indptr, x.causal) for x in c.chunks + [m])
+    flops = 2.0 * m.num_heads * pairs * 320
+    return {"workload": "chunked_prefill: 8 x (2048 new causal + 2 x 4096 context), 128 heads, "
+                        "3 prefill passes + 2 merge_state",
+            "ms_per_step": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
+            "flops_per_step": flops}
+
+
+def time_workload_prefill(mra, torch, x, steps, warmup, name):
+    plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, x.num_heads, x.causal).upload()
+    out = torch.empty((x.q.shape[0], x.num_heads, 128), dtype=x.q.dtype, device="cuda")
+    lse = torch.empty((x.q.shape[0], x.num_heads), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        plan.run(x.q, x.k, x.v, x.sm_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        plan.run(x.q, x.k, x.v, x.sm_scale, out=out, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * x.num_heads * visible_pairs(x.qo_indptr, x.kv_indptr, x.causal) * 320
+    return {"workload": name, "kernel_ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
+            "flops": flops}
+
+
+def time_decompress(mra, torch, workloads, steps, warmup):
+    d = workloads.decompress_batch(device="cuda")
+    H = d.num_heads
+    k, v = mra.decompress_kv(d.c_kv, d.k_rope, d.w_uk, d.w_uv, H)
+    for _ in range(warmup):
+        mra.decompress_kv(d.c_kv, d.k_rope, d.w_uk, d.w_uv, H, k_out=k, v_out=v)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mra.decompress_kv(d.c_kv, d.k_rope, d.w_uk, d.w_uv, H, k_out=k, v_out=v)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    t = d.c_kv.shape[0]
+    gemm_flops = 2.0 * 2 * t * 512 * H * 128
+    x = workloads.PrefillInputs(d.q, k, v, d.indptr, d.indptr, H, True, d.sm_scale)
+    pre = time_workload_prefill(mra, torch, x, steps, warmup, "prefill on the decompressed K/V")
+    return {"workload": "decompress_batch: 8 x 4096 tokens, latent 512 -> 128 heads (K_nope, V), "
+                        "then causal prefill",
+            "decompress_ms": round(ms, 4), "decompress_TFLOP/s": round(gemm_flops / ms / 1e9, 1),
+            "prefill_ms": pre["kernel_ms"], "prefill_TFLOP/s": pre["TFLOP/s"],
+            "end_to_end_ms": round(ms + pre["kernel_ms"], 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -209,6 +291,9 @@ def main():
         log(f"copied {n} bytes 3 times (read {n} B + write {n} B per copy)")
         return
     mra.lib()
+    if args.only == "merge":
+        print(json.dumps(time_merge(mra, torch, workloads, args.steps, args.warmup)), flush=True)
+        return
     t0 = time.perf_counter()
     x = workloads.deepseek_v3_batch(device="cuda")
     torch.cuda.synchronize()
@@ -251,13 +336,28 @@ def main():
                      "kernel": "prefill_bf16_kernel",
                      "kernel_ms": round(k_ms, 4)},
     }
-    if not args.no_secondary:
-        result["secondary"] = {"merge_state": time_merge(mra, torch, workloads, args.steps,
-                                                         args.warmup)}
     if args.cpu_seconds > 0:
         import oracle
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(oracle, torch, x, args.cpu_seconds)
+    if not args.no_secondary:
+        sec = {"merge_state": time_merge(mra, torch, workloads, args.steps, args.warmup)}
+        del x
+        torch.cuda.empty_cache()
+        log("secondary: chunked prefill ...")
+        sec["chunked_prefill"] = time_chunked(mra, torch, workloads, max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
+        log("secondary: skewed batch ...")
+        xs = workloads.skewed_batch(device="cuda")
+        sec["skewed_batch"] = time_workload_prefill(
+            mra, torch, xs, max(3, args.steps // 4), 1,
+            f"skewed_batch: 64 log-uniform lengths [16, 32768], {xs.qo_indptr[-1]} tokens, 128 heads")
+        del xs
+        torch.cuda.empty_cache()
+        log("secondary: decompression + prefill ...")
+        sec["decompress_batch"] = time_decompress(mra, torch, workloads, max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
+        result["secondary"] = sec
     print(json.dumps(result), flush=True)
 
 

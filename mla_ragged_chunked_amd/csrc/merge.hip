@@ -11,9 +11,11 @@
 // lse = -inf.
 //
 // Pure HBM streaming: every row of 128 values is read twice and written once.
-// Each lane moves 16 bytes per operand (8 bf16 or 4 fp32), the lanes of one
-// row sit in one wave (so an in-place LSE write cannot overtake a read of
-// the same row), and a grid-stride loop keeps several rows in flight per lane.
+// Each lane moves 16 bytes per operand (8 bf16 or 4 fp32) with non-temporal
+// loads and stores (the data is touched once), handles two rows' chunks per
+// iteration so both sets of loads are in flight together, and the lanes of
+// one row sit in one wave (so an in-place LSE write cannot overtake a read of
+// the same row: every lane of the wave has loaded before any lane stores).
 #include "internal.h"
 
 namespace mla {
@@ -36,56 +38,85 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 template <bool kBf16>
+__device__ __forceinline__ void merge_row_chunk(const u32x4_t xa, const u32x4_t xb, float a, float b,
+                                                u32x4_t& res, float& out_lse) {
+    const float mx = fmaxf(a, b);
+    float wa = 0.f, wb = 0.f;
+    out_lse = -INFINITY;
+    if (mx != -INFINITY) {
+        const float ea = __builtin_amdgcn_exp2f((a - mx) * kLog2e);   // exp(-inf) = 0
+        const float eb = __builtin_amdgcn_exp2f((b - mx) * kLog2e);
+        const float sum = ea + eb;
+        const float inv = 1.0f / sum;
+        wa = ea * inv;
+        wb = eb * inv;
+        out_lse = mx + __log2f(sum) * kLn2;
+    }
+    if constexpr (kBf16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float lo = 0.f, hi = 0.f;
+            if (wa != 0.f) { lo += wa * bf16_lo(xa[w]); hi += wa * bf16_hi(xa[w]); }
+            if (wb != 0.f) { lo += wb * bf16_lo(xb[w]); hi += wb * bf16_hi(xb[w]); }
+            res[w] = pack_bf16(lo, hi);
+        }
+    } else {
+        const f32x4_t fa = __builtin_bit_cast(f32x4_t, xa);
+        const f32x4_t fb = __builtin_bit_cast(f32x4_t, xb);
+        f32x4_t r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float x = 0.f;
+            if (wa != 0.f) x += wa * fa[w];
+            if (wb != 0.f) x += wb * fb[w];
+            r[w] = x;
+        }
+        res = __builtin_bit_cast(u32x4_t, r);
+    }
+}
+
+template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const void* __restrict__ o_a, const float* __restrict__ lse_a, const void* __restrict__ o_b,
     const float* __restrict__ lse_b, void* __restrict__ o, float* __restrict__ lse,
     int64_t num_rows) {
-    // lanes per row: 16 bytes of each operand per lane
     constexpr int kLanesPerRow = kBf16 ? kDvo * 2 / 16 : kDvo * 4 / 16;
+    constexpr int kUnroll = 2;      // two rows' chunks in flight per lane
     const int64_t total = num_rows * kLanesPerRow;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += stride) {
+    const u32x4_t* pa = reinterpret_cast<const u32x4_t*>(o_a);
+    const u32x4_t* pb = reinterpret_cast<const u32x4_t*>(o_b);
+    u32x4_t* po = reinterpret_cast<u32x4_t*>(o);
+    int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; idx + (kUnroll - 1) * stride < total; idx += kUnroll * stride) {
+        u32x4_t xa[kUnroll], xb[kUnroll];
+        float a[kUnroll], b[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = idx + u * stride;
+            const int64_t row = i / kLanesPerRow;
+            xa[u] = __builtin_nontemporal_load(pa + i);
+            xb[u] = __builtin_nontemporal_load(pb + i);
+            a[u] = lse_a[row];
+            b[u] = lse_b[row];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = idx + u * stride;
+            u32x4_t res;
+            float out_lse;
+            merge_row_chunk<kBf16>(xa[u], xb[u], a[u], b[u], res, out_lse);
+            __builtin_nontemporal_store(res, po + i);
+            if (i % kLanesPerRow == 0) lse[i / kLanesPerRow] = out_lse;
+        }
+    }
+    for (; idx < total; idx += stride) {
         const int64_t row = idx / kLanesPerRow;
-        const int c = (int)(idx % kLanesPerRow);
-        const float a = lse_a[row];
-        const float b = lse_b[row];
-        const u32x4_t xa = reinterpret_cast<const u32x4_t*>(o_a)[idx];
-        const u32x4_t xb = reinterpret_cast<const u32x4_t*>(o_b)[idx];
-        const float mx = fmaxf(a, b);
-        float wa = 0.f, wb = 0.f, out_lse = -INFINITY;
-        if (mx != -INFINITY) {
-            const float ea = __builtin_amdgcn_exp2f((a - mx) * kLog2e);   // exp(-inf) = 0
-            const float eb = __builtin_amdgcn_exp2f((b - mx) * kLog2e);
-            const float sum = ea + eb;
-            const float inv = 1.0f / sum;
-            wa = ea * inv;
-            wb = eb * inv;
-            out_lse = mx + __log2f(sum) * kLn2;
-        }
         u32x4_t res;
-        if constexpr (kBf16) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                float lo = 0.f, hi = 0.f;
-                if (wa != 0.f) { lo += wa * bf16_lo(xa[w]); hi += wa * bf16_hi(xa[w]); }
-                if (wb != 0.f) { lo += wb * bf16_lo(xb[w]); hi += wb * bf16_hi(xb[w]); }
-                res[w] = pack_bf16(lo, hi);
-            }
-        } else {
-            const f32x4_t fa = __builtin_bit_cast(f32x4_t, xa);
-            const f32x4_t fb = __builtin_bit_cast(f32x4_t, xb);
-            f32x4_t r;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                float x = 0.f;
-                if (wa != 0.f) x += wa * fa[w];
-                if (wb != 0.f) x += wb * fb[w];
-                r[w] = x;
-            }
-            res = __builtin_bit_cast(u32x4_t, r);
-        }
-        reinterpret_cast<u32x4_t*>(o)[idx] = res;
-        if (c == 0) lse[row] = out_lse;
+        float out_lse;
+        merge_row_chunk<kBf16>(pa[idx], pb[idx], lse_a[row], lse_b[row], res, out_lse);
+        po[idx] = res;
+        if (idx % kLanesPerRow == 0) lse[row] = out_lse;
     }
 }
 
@@ -97,8 +128,9 @@ hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b, co
     if (num_rows <= 0) return hipSuccess;
     const int64_t lanes_per_row = dtype_bf16 ? kDvo * 2 / 16 : kDvo * 4 / 16;
     const int64_t blocks_needed = (num_rows * lanes_per_row + kThreads - 1) / kThreads;
-    // enough waves to cover 256 CUs several times over; each lane loops
-    const int64_t max_blocks = 256 * 16;
+    // about one pass over the rows with two chunks per lane: a large grid
+    // keeps enough bytes in flight to stream at the HBM rate
+    const int64_t max_blocks = 256 * 256;
     const unsigned blocks = (unsigned)(blocks_needed < max_blocks ? blocks_needed : max_blocks);
     if (dtype_bf16)
         hipLaunchKernelGGL(merge_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, o_a, lse_a,
