@@ -187,7 +187,9 @@ def time_merge(mra, torch, workloads, steps, warmup):
     return {"workload": f"merge_state {tokens} tokens x {heads} heads, bf16",
             "kernel_ms": round(ms, 4), "GB/s": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": profile_traffic("merge_state_16384x128_bf16.txt",
+                                                    "mla_ragged_chunked_amd/csrc/merge.hip")}}
 
 
 def time_chunked(mra, torch, workloads, steps, warmup):
