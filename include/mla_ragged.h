@@ -119,9 +119,10 @@ void mla_plan_destroy(mla_plan *plan);
 
 /*
  * Build the work list on the host: the work partitioner splits every
- * sequence into query tiles, one work item per (sequence, head, query tile),
- * ordered so the heaviest groups go first and all tiles of one
- * (sequence, head) land on the same XCD. Validates like mla_ragged_prefill.
+ * sequence into query tiles, one work item per (query tile, block of
+ * consecutive heads) (see mla_plan_set_heads_per_item), ordered so the
+ * heaviest groups go first and all tiles of one (sequence, head block) land
+ * on the same XCD. Validates like mla_ragged_prefill.
  * Makes no HIP call, so it also runs on a machine without a GPU.
  * `dtype` selects the kernel (and so the query-tile height).
  */
@@ -144,22 +145,31 @@ int mla_ragged_run(const mla_plan *plan, const void *q, const void *k, const voi
 
 /*
  * Work-list inspection (host only): item count, and a copy of the items as
- * int32 [n, 8] = {q_row0, n_rows, head, kv_start, kv_len, diag0, kv_hi, seq}:
+ * int32 [n, 8] = {q_row0, n_rows, head0, n_heads, kv_start, kv_len, diag0, kv_hi}:
  *   q_row0   first query token of the tile (global index);
  *   n_rows   query rows in the tile (0 marks a padding item);
- *   head     head index;  kv_start first key token of the sequence;
- *   kv_len   keys in the sequence;
+ *   head0    first head of the item's head block;  n_heads heads in the block
+ *            (the kernel runs them one after the other);
+ *   kv_start first key token of the sequence;  kv_len keys in the sequence;
  *   diag0    row r of the tile sees keys < min(kv_len, max(0, diag0 + r + 1));
- *   kv_hi    keys the last row of the tile sees (the tile's loop bound);
- *   seq      sequence index.
- * `block_m` receives the query-tile height and `n_xcd` the XCD count used.
+ *   kv_hi    keys the last row of the tile sees (the loop bound per head).
+ * `block_m` receives the query-tile height, `n_xcd` the XCD count used and
+ * `heads_per_item` the head-block size (any pointer may be NULL).
  */
-int mla_plan_info(const mla_plan *plan, int64_t *n_items, int32_t *block_m, int32_t *n_xcd);
+int mla_plan_info(const mla_plan *plan, int64_t *n_items, int32_t *block_m, int32_t *n_xcd,
+                  int32_t *heads_per_item);
 int mla_plan_items(const mla_plan *plan, int32_t *dst, int64_t capacity_items);
 
 /* Number of XCDs the partitioner groups work for (default 8, MI355X; 1
  * turns the grouping off). Applies to later mla_ragged_plan calls. */
 int mla_plan_set_xcds(mla_plan *plan, int32_t n_xcd);
+
+/* Heads per work item (default 0: automatic, currently one head per item,
+ * the fastest measured choice at the MLA shapes). A nonzero value must
+ * divide num_heads, else mla_ragged_plan returns MLA_EINVAL; the kernel then
+ * runs that many consecutive heads of one query tile back to back. Applies
+ * to later mla_ragged_plan calls. */
+int mla_plan_set_heads_per_item(mla_plan *plan, int32_t heads_per_item);
 
 /*
  * merge_state: combine two attention states computed over disjoint key sets

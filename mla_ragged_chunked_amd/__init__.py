@@ -34,6 +34,7 @@ EXPORTED_SYMBOLS = [
     "mla_status_string", "mla_last_error", "mla_version", "mla_ragged_prefill",
     "mla_plan_create", "mla_plan_destroy", "mla_ragged_plan", "mla_plan_upload",
     "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_set_xcds",
+    "mla_plan_set_heads_per_item",
     "mla_merge_state", "mla_decompress_kv",
 ]
 
@@ -71,10 +72,11 @@ def lib():
         "mla_ragged_plan": ([P, P, P, I32, I32, I32, I32], ctypes.c_int),
         "mla_plan_upload": ([P, P], ctypes.c_int),
         "mla_ragged_run": ([P, P, P, P, F, I32, P, P, P], ctypes.c_int),
-        "mla_plan_info": ([P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32)],
-                          ctypes.c_int),
+        "mla_plan_info": ([P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32),
+                           ctypes.POINTER(I32)], ctypes.c_int),
         "mla_plan_items": ([P, P, I64], ctypes.c_int),
         "mla_plan_set_xcds": ([P, I32], ctypes.c_int),
+        "mla_plan_set_heads_per_item": ([P, I32], ctypes.c_int),
         "mla_merge_state": ([P, P, P, P, P, P, I64, I32, I32, P], ctypes.c_int),
         "mla_decompress_kv": ([P, P, P, P, I64, I32, P, P, P], ctypes.c_int),
     }
@@ -115,7 +117,7 @@ def _dev_tensor(t: torch.Tensor, name: str):
 class Plan:
     """Work list for one ragged batch: plan once (host), upload, run per layer."""
 
-    def __init__(self, n_xcd: Optional[int] = None):
+    def __init__(self, n_xcd: Optional[int] = None, heads_per_item: Optional[int] = None):
         l = lib()
         h = ctypes.c_void_p()
         _check(l.mla_plan_create(ctypes.byref(h)), "mla_plan_create")
@@ -123,6 +125,9 @@ class Plan:
         self._lib = l
         if n_xcd is not None:
             _check(l.mla_plan_set_xcds(h, int(n_xcd)), "mla_plan_set_xcds")
+        if heads_per_item is not None:
+            _check(l.mla_plan_set_heads_per_item(h, int(heads_per_item)),
+                   "mla_plan_set_heads_per_item")
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -151,10 +156,11 @@ class Plan:
         return self
 
     def info(self):
-        n, bm, nx = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        n, bm, nx, nh = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         _check(self._lib.mla_plan_info(self._h, ctypes.byref(n), ctypes.byref(bm),
-                                       ctypes.byref(nx)), "mla_plan_info")
-        return {"n_items": n.value, "block_m": bm.value, "n_xcd": nx.value}
+                                       ctypes.byref(nx), ctypes.byref(nh)), "mla_plan_info")
+        return {"n_items": n.value, "block_m": bm.value, "n_xcd": nx.value,
+                "heads_per_item": nh.value}
 
     def items(self) -> np.ndarray:
         n = self.info()["n_items"]

@@ -132,6 +132,7 @@ struct mla_plan {
     int64_t tq = 0, tk = 0;
     int32_t batch = 0, num_heads = 0, causal = 0, dtype = -1, block_m = 0;
     int32_t n_xcd = 8;
+    int32_t heads_per_item = 0;   // 0 = chosen by the planner
     bool planned = false;
     bool uploaded = false;
     DeviceWorkList dwl;
@@ -177,7 +178,8 @@ int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, in
     const int bm = dtype == MLA_DTYPE_BF16 ? mla::prefill_bf16_block_m() : mla::prefill_fp32_block_m();
     std::string err;
     try {
-        if (!mla::build_work_list(qo, kv, batch, heads, causal != 0, bm, p->n_xcd, p->items, err))
+        if (!mla::build_work_list(qo, kv, batch, heads, causal != 0, bm, p->n_xcd,
+                                  p->heads_per_item, p->items, err))
             return fail(MLA_EINVAL, err);
     } catch (const std::bad_alloc&) {
         return fail(MLA_ENOMEM, "host allocation of the work list failed");
@@ -278,12 +280,26 @@ int mla_ragged_run(const mla_plan* plan, const void* q, const void* k, const voi
     return do_run(plan, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream));
 }
 
-int mla_plan_info(const mla_plan* plan, int64_t* n_items, int32_t* block_m, int32_t* n_xcd) {
+int mla_plan_info(const mla_plan* plan, int64_t* n_items, int32_t* block_m, int32_t* n_xcd,
+                  int32_t* heads_per_item) {
     if (plan == nullptr) return fail(MLA_EINVAL, "plan is NULL");
     if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
     if (n_items) *n_items = static_cast<int64_t>(plan->items.size());
     if (block_m) *block_m = plan->block_m;
     if (n_xcd) *n_xcd = plan->n_xcd;
+    if (heads_per_item) {
+        int32_t nh = 0;
+        for (const WorkItem& w : plan->items)
+            if (w.n_rows > 0) { nh = w.n_heads; break; }
+        *heads_per_item = nh;
+    }
+    return MLA_OK;
+}
+
+int mla_plan_set_heads_per_item(mla_plan* plan, int32_t heads_per_item) {
+    if (plan == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (heads_per_item < 0) return fail(MLA_EINVAL, "heads_per_item must be >= 0");
+    plan->heads_per_item = heads_per_item;
     return MLA_OK;
 }
 

@@ -15,19 +15,20 @@ constexpr int kDlat = 512;
 constexpr int kDrope = 64;
 constexpr int kDnope = 128;
 
-// One work item = one query tile of one (sequence, head). 32 bytes.
+// One work item = one query tile of one sequence for a block of heads
+// [head0, head0 + n_heads), processed one head after the other. 32 bytes.
 //   row r of the tile (0 <= r < n_rows) sees keys [0, lim(r)) of its sequence,
 //   lim(r) = min(kv_len, max(0, diag0 + r + 1)).
 // Non-causal tiles carry diag0 = kv_len, so lim(r) = kv_len.
 struct WorkItem {
     int32_t q_row0;    // global token index of the tile's first query row
     int32_t n_rows;    // rows in the tile; 0 = padding item (kernel returns)
-    int32_t head;
+    int32_t head0;     // first head of the block
+    int32_t n_heads;   // heads in the block (>= 1 for a real item)
     int32_t kv_start;  // global token index of the sequence's first key
     int32_t kv_len;
     int32_t diag0;
-    int32_t kv_hi;     // lim(n_rows - 1): keys the tile must visit
-    int32_t seq;
+    int32_t kv_hi;     // lim(n_rows - 1): keys the tile must visit (per head)
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
 
@@ -39,8 +40,11 @@ int prefill_fp32_block_m();
 // Build the ordered work list (host only). Returns false with `err` set on
 // invalid input. `block_m` is the query-tile height, `n_xcd` the number of
 // XCDs work is grouped for (1 = no grouping).
+// `heads_per_item` is the head-block size (it must divide num_heads); 0
+// picks one: the largest of 8, 4, 2, 1 that divides num_heads and still
+// leaves at least kMinItemsPerSlot items for every workgroup slot.
 bool build_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
-                     int num_heads, bool causal, int block_m, int n_xcd,
+                     int num_heads, bool causal, int block_m, int n_xcd, int heads_per_item,
                      std::vector<WorkItem>& out, std::string& err);
 
 // Kernel launchers (one kernel each, enqueued on `stream`).

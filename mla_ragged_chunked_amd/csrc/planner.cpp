@@ -4,18 +4,23 @@
 // layer ("vllm.v1.attention.backends.mla.prefill.flashinfer",
 // finalize_attention_metadata: plan() with kv_indptr = qo_indptr for the
 // causal pass and kv_indptr = cu_seq_lens[i] for each context chunk).
-// This partitioner turns those indptrs into one work item per
-// (sequence, head, query tile), ordered for the MI355X:
+// This partitioner turns those indptrs into work items, ordered for the
+// MI355X:
 //
-//  1. A tile of `block_m` query rows needs keys [0, kv_hi) of its sequence,
-//     kv_hi from the bottom-right causal rule (or kv_len when non-causal);
-//     its cost is kv_hi plus a fixed charge for loading Q and writing O.
-//  2. All tiles of one (sequence, head) form a group: they read the same K/V
-//     rows, so they should share one XCD's L2. Groups are dealt to the XCD
-//     bins heaviest first, each to the currently lightest bin (LPT).
-//  3. Each bin lists its groups heaviest first and, inside a group, its
+//  1. A sequence is cut into query tiles of `block_m` rows. A tile needs keys
+//     [0, kv_hi) of its sequence, kv_hi from the bottom-right causal rule (or
+//     kv_len when non-causal); its cost per head is kv_hi plus a fixed charge
+//     for loading Q and writing O.
+//  2. One work item is one query tile for a block of consecutive heads
+//     (one head unless the caller asks for more): the kernel runs the heads
+//     one after the other with its K/V pipeline streaming straight from one
+//     head into the next.
+//  3. All tiles of one (sequence, head block) form a group: they read the
+//     same K/V rows, so they should share one XCD's L2. Groups are dealt to
+//     the XCD bins heaviest first, each to the currently lightest bin (LPT).
+//  4. Each bin lists its groups heaviest first and, inside a group, its
 //     tiles heaviest first, so long tiles start early and the tail is short.
-//  4. The hardware hands workgroup i to XCD i mod n_xcd, so bin x's s-th item
+//  5. The hardware hands workgroup i to XCD i mod n_xcd, so bin x's s-th item
 //     is placed at index s * n_xcd + x; shorter bins are padded with
 //     empty items (n_rows = 0) that the kernel skips.
 #include <algorithm>
@@ -35,13 +40,17 @@ struct Tile {
 }  // namespace
 
 bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_heads,
-                     bool causal, int block_m, int n_xcd, std::vector<WorkItem>& out,
-                     std::string& err) {
+                     bool causal, int block_m, int n_xcd, int heads_per_item,
+                     std::vector<WorkItem>& out, std::string& err) {
     out.clear();
     if (batch < 0) { err = "batch must be >= 0"; return false; }
     if (num_heads < 1 || num_heads > 65535) { err = "num_heads must be in [1, 65535]"; return false; }
     if (block_m < 1) { err = "block_m must be >= 1"; return false; }
     if (n_xcd < 1 || n_xcd > 64) { err = "n_xcd must be in [1, 64]"; return false; }
+    if (heads_per_item < 0 || (heads_per_item > 0 && num_heads % heads_per_item != 0)) {
+        err = "heads_per_item must be 0 (automatic) or divide num_heads";
+        return false;
+    }
     if (batch == 0) return true;
     if (qo == nullptr || kv == nullptr) { err = "indptr pointer is NULL"; return false; }
     if (qo[0] != 0 || kv[0] != 0) { err = "indptr[0] must be 0"; return false; }
@@ -78,15 +87,21 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
     }
     if (tiles.empty()) return true;
 
-    // Groups = (sequence, head), all heads of a sequence cost the same.
-    struct Group { int32_t seq, head; int64_t cost; };
+    // Head blocks are a caller's choice; measured on MI355X, one head per
+    // item is never slower at the MLA shapes (the next head's Q load cannot be
+    // issued early enough to hide its latency, and bigger items balance worse).
+    const int nh = heads_per_item == 0 ? 1 : heads_per_item;
+    const int n_blocks = num_heads / nh;
+
+    // Groups = (sequence, head block); all blocks of a sequence cost the same.
+    struct Group { int32_t seq, head0; int64_t cost; };
     std::vector<Group> groups;
-    groups.reserve(static_cast<size_t>(batch) * num_heads);
+    groups.reserve(static_cast<size_t>(batch) * n_blocks);
     for (int b = 0; b < batch; ++b) {
         if (seq_tiles[b].first == seq_tiles[b].second) continue;
         int64_t c = 0;
         for (size_t i = seq_tiles[b].first; i < seq_tiles[b].second; ++i) c += tiles[i].cost;
-        for (int h = 0; h < num_heads; ++h) groups.push_back({b, h, c});
+        for (int hb = 0; hb < n_blocks; ++hb) groups.push_back({b, hb * nh, c * nh});
     }
     std::stable_sort(groups.begin(), groups.end(),
                      [](const Group& a, const Group& c) { return a.cost > c.cost; });
@@ -115,12 +130,12 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
                 WorkItem& w = out[s * n_xcd + x];
                 w.q_row0 = t.q_row0;
                 w.n_rows = t.n_rows;
-                w.head = g->head;
+                w.head0 = g->head0;
+                w.n_heads = nh;
                 w.kv_start = t.kv_start;
                 w.kv_len = t.kv_len;
                 w.diag0 = t.diag0;
                 w.kv_hi = t.kv_hi;
-                w.seq = t.seq;
             }
         }
     }

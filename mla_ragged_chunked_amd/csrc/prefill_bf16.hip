@@ -1,7 +1,7 @@
 // Ragged MLA prefill attention, bf16 inputs, for gfx950 (CDNA4).
 //
-// Computes, per work item (one query tile of one (sequence, head)), flash-
-// style attention with Dqk = 192 and Dvo = 128: S = sm_scale * Q K^T over the
+// Computes, per work item (one query tile of one sequence, for a block of
+// consecutive heads run one after the other), flash-style attention with Dqk = 192 and Dvo = 128: S = sm_scale * Q K^T over the
 // visible keys (bottom-right causal or all), online softmax in fp32, O = P V,
 // and the natural-log LSE per row. This is the ragged prefill of
 // "vllm.v1.attention.backends.mla.prefill.flashinfer" (run() with
@@ -14,7 +14,7 @@
 //    each), so one wave's VALU work also overlaps the other wave's MFMAs.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from LDS, B = 16 dims x
-//    32 queries (Q stays in VGPRs for the whole item). In the accumulator
+//    32 queries (Q stays in VGPRs for the whole head). In the accumulator
 //    each lane owns one query column and 16 keys, so row max / row sum are
 //    in-lane plus one v_permlane32_swap between the two 32-lane halves.
 //  * That accumulator, rounded to bf16, is directly the B operand of
@@ -31,7 +31,10 @@
 //    MFMA fragment reads are bank-conflict free; V rows are 256 B with an XOR
 //    swizzle of their chunks for the transposing reads. Addresses are a
 //    per-tile scalar base plus a per-lane 32-bit offset computed once per
-//    item (recomputed with a clamp only on a sequence's last tile).
+//    item (recomputed with a clamp only on a sequence's last tile). The ring
+//    runs on from one head of the item into the next without draining, and
+//    the next head's Q is loaded during the current head's last tile, so the
+//    start-up latency is paid once per item rather than once per head.
 //  * Software pipeline, one barrier per tile: iteration j publishes tile j+1
 //    (and retires tile j-1), puts tile j+3 in flight into tile j-1's stage,
 //    computes the scores of tile j+1 and runs softmax + PV of tile j, so
@@ -76,6 +79,9 @@ constexpr int kKBlocksPerWave = (kKBytes / 1024) / kWaves;   // 3
 constexpr int kVBlocksPerWave = (kVBytes / 1024) / kWaves;   // 2
 constexpr int kLoadsPerTile = kKBlocksPerWave + kVBlocksPerWave;
 constexpr float kLazyRescale = 8.0f;
+// s_waitcnt immediate that waits for vmcnt = 0 only (expcnt and lgkmcnt
+// fields at their maxima, gfx9 encoding)
+constexpr int kVmcnt0 = (0x7 << 4) | (0xf << 8);
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float xor32_max(float x) {
@@ -143,15 +149,14 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     bf16x8_t qf[kKSteps];
     const int my_row = row_w0 + l32;
     const int my_lim = lim_of(my_row, it.diag0, it.kv_len);
-    if (my_row < it.n_rows) {
-        const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(
-            q + ((int64_t)(it.q_row0 + my_row) * H + it.head) * kDqk);
+    // Rows past the tile's end load its last row instead (their results
+    // are never stored), so every lane loads and no lane needs zero-filling.
+    const int q_row = it.q_row0 + (my_row < it.n_rows ? my_row : it.n_rows - 1);
+    auto load_q = [&](int head, bf16x8_t (&dst)[kKSteps]) {
+        const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(q + ((int64_t)q_row * H + head) * kDqk);
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) qf[s] = src[s * 2 + g];
-    } else {
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s) qf[s] = bf16x8_t{};
-    }
+        for (int s = 0; s < kKSteps; ++s) dst[s] = src[s * 2 + g];
+    };
 
     f32x16_t oacc[4];
 #pragma unroll
@@ -165,7 +170,7 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     // V: 8 blocks of 4 rows x 256 B; row r's chunk c sits at slot vslot(r, c).
     // Keys at or past kv_len load the last valid row instead (finite data;
     // the mask gives those keys p = 0).
-    const int64_t kv_row0 = (int64_t)it.kv_start * H + it.head;   // row index of key 0
+    const int64_t kv_row0 = (int64_t)it.kv_start * H;   // row index of key 0, head 0
     const int last_key = it.kv_len - 1;
     // Per-lane byte offsets (from the tile's first key row) of this wave's
     // loads: 3 K blocks and 2 V blocks; recomputed with the clamp only on a
@@ -194,12 +199,13 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         ld_off[j] = (uint32_t)ld_row[j] * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
     const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k + kv_row0 * kDqk);
     const uint8_t* vseq = reinterpret_cast<const uint8_t*>(v + kv_row0 * kDvo);
-    auto issue_tile = [&](int kt, int stage) {
+    // Tile kt of head `head` into `stage`.
+    auto issue_tile = [&](int head, int kt, int stage) {
         uint8_t* ks = smem + stage * kStage;
         uint8_t* vs = ks + kKBytes;
         const int key0 = kt * kBN;
-        const uint8_t* kb = kseq + (uint64_t)key0 * krow;
-        const uint8_t* vb = vseq + (uint64_t)key0 * vrow;
+        const uint8_t* kb = kseq + ((uint64_t)key0 * H + head) * (kDqk * 2);
+        const uint8_t* vb = vseq + ((uint64_t)key0 * H + head) * (kDvo * 2);
         uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
         if (key0 + kBN - 1 > last_key) {
             const int lim = last_key - key0;
@@ -255,16 +261,26 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     // V^T fragment for dv block db, key step mm (16 keys): two transposing
     // reads of 4 keys each. Lane (g, h = bit 4, j = low 4 bits, r = j/4,
     // q = j%4) supplies row mm*16 + t*8 + g*4 + r, dims db*32 + h*16 + 4q.
-    const int tr_h = (lane >> 4) & 1;
-    const int tr_r = (lane & 15) >> 2;
-    const int tr_q = lane & 3;
-    auto vfrag = [&](const uint8_t* vs, int db, int mm) {
+    // The swizzle only depends on row % 4 = r, so the per-lane offset of
+    // (db, mm = 0, t = 0) is computed once and (mm, t) become immediates.
+    int v_off[4];
+    {
+        const int tr_h = (lane >> 4) & 1;
+        const int tr_r = (lane & 15) >> 2;
+        const int tr_q = lane & 3;
+        const int row = g * 4 + tr_r;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const int chunk = db * 4 + tr_h * 2 + (tr_q >> 1);
+            v_off[db] = kKBytes + row * 256 + vslot(row, chunk) * 16 + (tr_q & 1) * 8;
+        }
+    }
+    auto vfrag = [&](const uint8_t* st, int db, int mm) {
         bf16x8_t a;
+        const uint8_t* base = st + v_off[db];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int row = mm * 16 + t * 8 + g * 4 + tr_r;
-            const int chunk = db * 4 + tr_h * 2 + (tr_q >> 1);
-            const uint8_t* p = vs + row * 256 + vslot(row, chunk) * 16 + (tr_q & 1) * 8;
+            const uint8_t* p = base + (mm * 16 + t * 8) * 256;
             const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
             const bf16x4_t y = __builtin_bit_cast(bf16x4_t, x);
             a[t * 4 + 0] = y[0];
@@ -275,7 +291,7 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         return a;
     };
     auto accumulate = [&](int stage, const f32x16_t& sacc) {
-        const uint8_t* vs = smem + stage * kStage + kKBytes;
+        const uint8_t* st = smem + stage * kStage;
         bf16x8_t pf[2];
         const float msub = m_run == -INFINITY ? 0.0f : m_run;
         float lsum = l_run;
@@ -298,91 +314,148 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
-                const bf16x8_t a = vfrag(vs, db, mm);
+                const bf16x8_t a = vfrag(st, db, mm);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[mm], oacc[db], 0, 0, 0);
             }
         }
     };
 
+    // O = acc / l and LSE = (m + log2 l) ln 2 for head `head` (waves with rows)
+    auto store_out = [&](int head) {
+        if (wave_rows <= 0) return;
+        const float ltot = xor32_sum(l_run);
+        if (my_row >= it.n_rows) return;
+        const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
+        const int64_t orow = (int64_t)(it.q_row0 + my_row) * H + head;
+        uint16_t* dst = out + orow * kDvo;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int dv = db * 32 + grp * 8 + g * 4;
+                bf16x4_t o4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][grp * 4 + e] * inv);
+                *reinterpret_cast<bf16x4_t*>(dst + dv) = o4;
+            }
+        }
+        if (g == 0 && lse != nullptr)
+            lse[orow] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
+    };
+
+    // Tiles per head; the item's heads run one after the other and the K/V
+    // ring streams on across head boundaries: global tile g = h * n_tiles + kt
+    // (h = head index in the block) lives in stage g % kStages.
     const int n_tiles = (it.kv_hi + kBN - 1) / kBN;
+    const int n_heads = it.n_heads;
+    const int total_tiles = n_tiles * n_heads;
     const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
     const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
 
-    // Software pipeline: iteration j computes the scores of tile j+1 (K of
-    // stage (j+1)%4) while it runs the softmax and PV of tile j (V of stage
-    // j%4), so each wave always has independent MFMA and VALU work. Loads run
-    // two tiles ahead of the K use.
-    //   top of iteration j: wait for this wave's loads of tile j+1, barrier
-    //   (publishes tile j+1 and retires tile j-1), put tile j+3 in flight
-    //   into tile j-1's stage.
-    auto sync_top = [&](int j) {
-        // loads issued so far: tiles 0 .. j+2; tile j+1 must be complete
-        if (j + 2 < n_tiles) wait_vmcnt<kLoadsPerTile>();
+    // issue cursor: the next global tile to put in flight
+    int iss_g = 0, iss_h = 0, iss_kt = 0;
+    auto issue_next = [&]() {
+        issue_tile(it.head0 + iss_h, iss_kt, iss_g % kStages);
+        ++iss_g;
+        if (++iss_kt == n_tiles) { iss_kt = 0; ++iss_h; }
+    };
+    // Software pipeline: the iteration for global tile g publishes tile g+1
+    // (one barrier; it also retires tile g-1), puts tile g+3 in flight into
+    // tile g-1's stage, computes the scores of the next tile of the same head
+    // and runs softmax + PV of tile g.
+    auto sync_top = [&](int gt) {
+        // loads issued so far: tiles 0 .. gt+2; tile gt+1 must be complete
+        if (gt + 2 < total_tiles) wait_vmcnt<kLoadsPerTile>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (j + 3 < n_tiles) issue_tile(j + 3, (j + 3) % kStages);
+        if (gt + 3 < total_tiles) issue_next();
     };
 
-#pragma unroll
-    for (int t = 0; t < 3; ++t)
-        if (t < n_tiles) issue_tile(t, t);
-    // tile 0 must be complete: tiles 1 and 2 may still be in flight
-    if (n_tiles > 2) wait_vmcnt<2 * kLoadsPerTile>();
-    else if (n_tiles > 1) wait_vmcnt<kLoadsPerTile>();
+    // A wave whose rows see no key never reads Q.
+    if (n_wave > 0) load_q(it.head0, qf);
+    for (int t = 0; t < 3 && t < total_tiles; ++t) issue_next();
+    // Q and tile 0 must be complete: tiles 1 and 2 may still be in flight
+    if (total_tiles > 2) wait_vmcnt<2 * kLoadsPerTile>();
+    else if (total_tiles > 1) wait_vmcnt<kLoadsPerTile>();
     else wait_vmcnt<0>();
     __syncthreads();
 
-    f32x16_t s_cur;
-    if (n_wave > 0) {
-        if (n_full > 0) scores(0, 0, std::false_type{}, s_cur);
-        else scores(0, 0, std::true_type{}, s_cur);
-    }
-    // one pipelined iteration; kNext: 0 = no next tile, 1 = unmasked, 2 = masked
-    auto iteration = [&](int j, auto next_kind) {
-        constexpr int kNext = decltype(next_kind)::value;
-        sync_top(j);
-        const float mt = tile_max(s_cur);
-        if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+    for (int h = 0; h < n_heads; ++h) {
+        const int gbase = h * n_tiles;
+        const bool more_heads = h + 1 < n_heads;
+        int j = 0;
+        if (n_wave > 0) {
 #pragma unroll
-            for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+            m_run = -INFINITY;
+            l_run = 0.f;
+            // One pipelined iteration: consumes the scores of tile j in s_cur
+            // and, unless kNext == 0, leaves those of tile j + 1 in s_nxt
+            // (kNext: 0 = no next tile, 1 = unmasked, 2 = masked). The loops
+            // below alternate two score buffers, so nothing is copied.
+            auto iteration = [&](int jj, auto next_kind, const f32x16_t& s_cur, f32x16_t& s_nxt) {
+                constexpr int kNext = decltype(next_kind)::value;
+                const int gt = gbase + jj;
+                sync_top(gt);
+                if constexpr (kNext == 0) {
+                    // The next head's Q: issued after this tile's DMA, so
+                    // waiting for it later never waits on a younger tile.
+                    if (more_heads) load_q(it.head0 + h + 1, qf);
+                }
+                const float mt = tile_max(s_cur);
+                if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
+                    const float m_new = fmaxf(m_run, mt);
+                    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+                }
+                if constexpr (kNext == 1) scores(jj + 1, (gt + 1) % kStages, std::false_type{}, s_nxt);
+                if constexpr (kNext == 2) scores(jj + 1, (gt + 1) % kStages, std::true_type{}, s_nxt);
+                accumulate(gt % kStages, s_cur);
+            };
+            // The first tile always takes the masked form (a no-op on a fully
+            // visible tile): one straight-line path into the loops, on which
+            // the compiler sees the Q wait.
+            f32x16_t sa, sb;
+            scores(0, gbase % kStages, std::true_type{}, sa);
+            // tiles j with an unmasked successor, then with a masked one
+            for (; j + 2 < n_full; j += 2) {
+                iteration(j, std::integral_constant<int, 1>{}, sa, sb);
+                iteration(j + 1, std::integral_constant<int, 1>{}, sb, sa);
+            }
+            if (j + 1 < n_full) {
+                iteration(j, std::integral_constant<int, 1>{}, sa, sb);
+                sa = sb;
+                ++j;
+            }
+            for (; j + 2 < n_wave; j += 2) {
+                iteration(j, std::integral_constant<int, 2>{}, sa, sb);
+                iteration(j + 1, std::integral_constant<int, 2>{}, sb, sa);
+            }
+            if (j + 1 < n_wave) {
+                iteration(j, std::integral_constant<int, 2>{}, sa, sb);
+                sa = sb;
+                ++j;
+            }
+            iteration(j, std::integral_constant<int, 0>{}, sa, sb);
+            ++j;
+            // The next head's Q loads are the youngest vector-memory reads:
+            // completing them here costs no ring tile. The empty asm then
+            // redefines the Q registers, so the compiler no longer sees loads
+            // in flight into them and puts no waits of its own in the loops.
+            if (more_heads) {
+                __builtin_amdgcn_s_waitcnt(kVmcnt0);
+#pragma unroll
+                for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+v"(qf[s]));
+            }
         }
-        f32x16_t s_next;
-        if constexpr (kNext == 1) scores(j + 1, (j + 1) % kStages, std::false_type{}, s_next);
-        if constexpr (kNext == 2) scores(j + 1, (j + 1) % kStages, std::true_type{}, s_next);
-        accumulate(j % kStages, s_cur);
-        if constexpr (kNext != 0) s_cur = s_next;
-    };
-    int j = 0;
-    for (; j + 1 < n_full; ++j) iteration(j, std::integral_constant<int, 1>{});
-    for (; j + 1 < n_wave; ++j) iteration(j, std::integral_constant<int, 2>{});
-    if (j < n_wave) { iteration(j, std::integral_constant<int, 0>{}); ++j; }
-    for (; j < n_tiles; ++j) sync_top(j);
+        store_out(it.head0 + h);
+        // tiles only other waves need: barriers and loads
+        for (; j < n_tiles; ++j) sync_top(gbase + j);
+    }
     wait_vmcnt<0>();
-
-    // ---- epilogue
-    if (wave_rows <= 0) return;
-    const float ltot = xor32_sum(l_run);
-    if (my_row >= it.n_rows) return;
-    const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
-    const int64_t orow = (int64_t)(it.q_row0 + my_row) * H + it.head;
-    uint16_t* dst = out + orow * kDvo;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-            const int dv = db * 32 + grp * 8 + g * 4;
-            bf16x4_t o4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][grp * 4 + e] * inv);
-            *reinterpret_cast<bf16x4_t*>(dst + dv) = o4;
-        }
-    }
-    if (g == 0 && lse != nullptr)
-        lse[orow] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

@@ -7,7 +7,8 @@
 // accuracy (fp32 callers, the 1e-4 / 1e-5 bounds); the bf16 MFMA kernel is
 // the throughput path.
 //
-// One wave per work item, one query row per lane (64-row tiles). K and V
+// One wave per work item (its heads one after the other), one query row per
+// lane (64-row tiles). K and V
 // tiles of 32 keys are staged in LDS and read as broadcasts (all lanes read
 // the same key), scores for the tile are kept in registers, then one
 // online-softmax update per tile.
@@ -38,71 +39,73 @@ __global__ __launch_bounds__(kThreads) void prefill_fp32_kernel(
     int lim = it.diag0 + lane + 1;
     lim = lim < 0 ? 0 : (lim > it.kv_len ? it.kv_len : lim);
 
-    float qv[kDqk];
-    const int64_t qrow = (int64_t)(it.q_row0 + lane) * H + it.head;
+    for (int head = it.head0; head < it.head0 + it.n_heads; ++head) {
+        float qv[kDqk];
+        const int64_t qrow = (int64_t)(it.q_row0 + lane) * H + head;
 #pragma unroll
-    for (int d = 0; d < kDqk; d += 4) {
-        f32x4_t x = valid ? *reinterpret_cast<const f32x4_t*>(q + qrow * kDqk + d) : f32x4_t{};
-        qv[d] = x[0]; qv[d + 1] = x[1]; qv[d + 2] = x[2]; qv[d + 3] = x[3];
-    }
-    float o[kDvo];
+        for (int d = 0; d < kDqk; d += 4) {
+            f32x4_t x = valid ? *reinterpret_cast<const f32x4_t*>(q + qrow * kDqk + d) : f32x4_t{};
+            qv[d] = x[0]; qv[d + 1] = x[1]; qv[d + 2] = x[2]; qv[d + 3] = x[3];
+        }
+        float o[kDvo];
 #pragma unroll
-    for (int d = 0; d < kDvo; ++d) o[d] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    const int64_t kv_base = (int64_t)it.kv_start * H + it.head;
+        for (int d = 0; d < kDvo; ++d) o[d] = 0.f;
+        float m_run = -INFINITY, l_run = 0.f;
+        const int64_t kv_base = (int64_t)it.kv_start * H + head;
 
-    for (int key0 = 0; key0 < it.kv_hi; key0 += kBN) {
-        __syncthreads();
-        for (int u = lane; u < kBN * (kDqk / 4); u += kThreads) {
-            const int row = u / (kDqk / 4), c = u % (kDqk / 4);
-            const int key = key0 + row;
-            *reinterpret_cast<f32x4_t*>(&ks[row][c * 4]) =
-                key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(k + (kv_base + (int64_t)key * H) * kDqk + c * 4)
-                                : f32x4_t{};
-        }
-        for (int u = lane; u < kBN * (kDvo / 4); u += kThreads) {
-            const int row = u / (kDvo / 4), c = u % (kDvo / 4);
-            const int key = key0 + row;
-            *reinterpret_cast<f32x4_t*>(&vs[row][c * 4]) =
-                key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(v + (kv_base + (int64_t)key * H) * kDvo + c * 4)
-                                : f32x4_t{};
-        }
-        __syncthreads();
+        for (int key0 = 0; key0 < it.kv_hi; key0 += kBN) {
+            __syncthreads();
+            for (int u = lane; u < kBN * (kDqk / 4); u += kThreads) {
+                const int row = u / (kDqk / 4), c = u % (kDqk / 4);
+                const int key = key0 + row;
+                *reinterpret_cast<f32x4_t*>(&ks[row][c * 4]) =
+                    key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(k + (kv_base + (int64_t)key * H) * kDqk + c * 4)
+                                    : f32x4_t{};
+            }
+            for (int u = lane; u < kBN * (kDvo / 4); u += kThreads) {
+                const int row = u / (kDvo / 4), c = u % (kDvo / 4);
+                const int key = key0 + row;
+                *reinterpret_cast<f32x4_t*>(&vs[row][c * 4]) =
+                    key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(v + (kv_base + (int64_t)key * H) * kDvo + c * 4)
+                                    : f32x4_t{};
+            }
+            __syncthreads();
 
-        float s[kBN];
-        float mx = -INFINITY;
+            float s[kBN];
+            float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kBN; ++j) {
-            float dot = 0.f;
+            for (int j = 0; j < kBN; ++j) {
+                float dot = 0.f;
 #pragma unroll
-            for (int d = 0; d < kDqk; ++d) dot = __builtin_fmaf(qv[d], ks[j][d], dot);
-            s[j] = key0 + j < lim ? dot * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, s[j]);
+                for (int d = 0; d < kDqk; ++d) dot = __builtin_fmaf(qv[d], ks[j][d], dot);
+                s[j] = key0 + j < lim ? dot * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, s[j]);
+            }
+            const float m_new = fmaxf(m_run, mx);
+            const float msub = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - msub);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < kDvo; ++d) o[d] *= alpha;
+#pragma unroll
+            for (int j = 0; j < kBN; ++j) {
+                const float p = __builtin_amdgcn_exp2f(s[j] - msub);
+                l_run += p;
+#pragma unroll
+                for (int d = 0; d < kDvo; ++d) o[d] = __builtin_fmaf(p, vs[j][d], o[d]);
+            }
         }
-        const float m_new = fmaxf(m_run, mx);
-        const float msub = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - msub);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < kDvo; ++d) o[d] *= alpha;
-#pragma unroll
-        for (int j = 0; j < kBN; ++j) {
-            const float p = __builtin_amdgcn_exp2f(s[j] - msub);
-            l_run += p;
-#pragma unroll
-            for (int d = 0; d < kDvo; ++d) o[d] = __builtin_fmaf(p, vs[j][d], o[d]);
-        }
-    }
 
-    if (!valid) return;
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+        if (!valid) continue;
+        const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
 #pragma unroll
-    for (int d = 0; d < kDvo; d += 4) {
-        f32x4_t x = {o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
-        *reinterpret_cast<f32x4_t*>(out + qrow * kDvo + d) = x;
+        for (int d = 0; d < kDvo; d += 4) {
+            f32x4_t x = {o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
+            *reinterpret_cast<f32x4_t*>(out + qrow * kDvo + d) = x;
+        }
+        if (lse != nullptr) lse[qrow] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
     }
-    if (lse != nullptr) lse[qrow] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

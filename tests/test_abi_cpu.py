@@ -1,6 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol the
 header declares, rejects invalid arguments with a status before touching the
-device, and its work partitioner covers every (sequence, head, row) once."""
+device, and its work partitioner covers every (token, head) once."""
 import ctypes
 import os
 import re
@@ -112,18 +112,25 @@ def _lim(r, diag0, kv_len):
     return min(kv_len, max(0, diag0 + r + 1))
 
 
-def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8):
+def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8, heads_per_item=None):
     import torch
-    p = mra.Plan(n_xcd=n_xcd)
+    p = mra.Plan(n_xcd=n_xcd, heads_per_item=heads_per_item)
     p.plan(qo, kv, heads, causal, torch.bfloat16 if dtype_name == "bf16" else torch.float32)
     info = p.info()
     items = p.items()
     bm = info["block_m"]
+    nh = info["heads_per_item"]
     real = items[items[:, 1] > 0]
+    if len(real):
+        assert heads % nh == 0
+        if heads_per_item:
+            assert nh == heads_per_item
     # every (token, head) exactly once
     cover = np.zeros((qo[-1], heads), dtype=np.int64)
-    for (q_row0, n_rows, head, kv_start, kv_len, diag0, kv_hi, seq) in real:
+    for (q_row0, n_rows, head0, n_heads, kv_start, kv_len, diag0, kv_hi) in real:
+        seq = int(np.searchsorted(qo, q_row0, side="right")) - 1
         assert 0 < n_rows <= bm
+        assert n_heads == nh and head0 % nh == 0 and 0 <= head0 and head0 + n_heads <= heads
         assert qo[seq] <= q_row0 and q_row0 + n_rows <= qo[seq + 1]     # inside its sequence
         assert (q_row0 - qo[seq]) % bm == 0
         assert kv_start == kv[seq] and kv_len == kv[seq + 1] - kv[seq]
@@ -132,17 +139,20 @@ def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8):
         want_diag0 = kv_len - qo_len + r0 if causal else kv_len
         assert diag0 == want_diag0
         assert kv_hi == _lim(n_rows - 1, diag0, kv_len)
-        cover[q_row0:q_row0 + n_rows, head] += 1
+        cover[q_row0:q_row0 + n_rows, head0:head0 + n_heads] += 1
     assert np.all(cover == 1)
-    # XCD grouping: all tiles of one (sequence, head) share index mod n_xcd
+    # XCD grouping: all tiles of one (sequence, head block) share index mod n_xcd
     idx = np.nonzero(items[:, 1] > 0)[0]
     groups = {}
     for i in idx:
-        key = (items[i, 7], items[i, 2])
-        groups.setdefault(key, set()).add(i % n_xcd)
+        groups.setdefault(_group(qo, items[i]), set()).add(i % n_xcd)
     assert all(len(v) == 1 for v in groups.values())
     assert len(items) % n_xcd == 0
     return items, info
+
+
+def _group(qo, it):
+    return int(np.searchsorted(qo, it[0], side="right")) - 1, int(it[2])
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -150,6 +160,8 @@ def test_partition_covers_every_row_once(causal):
     lens = [1, 17, 64, 300, 257, 0, 1000]
     qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     _check_plan(qo, qo, 3, causal)
+    _check_plan(qo, qo, 8, causal, heads_per_item=4)
+    _check_plan(qo, qo, 8, causal, dtype_name="fp32", heads_per_item=8)
 
 
 def test_partition_handles_ragged_edges():
@@ -159,31 +171,51 @@ def test_partition_handles_ragged_edges():
     qo = np.concatenate([[0], np.cumsum(qo_lens)]).astype(np.int32)
     kv = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
     items, _ = _check_plan(qo, kv, 2, True)
-    # the tile of the kv = 0 sequence has nothing to visit
-    s1 = items[(items[:, 7] == 1) & (items[:, 1] > 0)]
-    assert np.all(s1[:, 6] == 0)
+    # the tiles of the kv = 0 sequence have nothing to visit
+    s1 = np.array([it for it in items if it[1] > 0 and _group(qo, it)[0] == 1])
+    assert len(s1) and np.all(s1[:, 7] == 0)
     _check_plan(qo, kv, 2, False, dtype_name="fp32")
+    _check_plan(qo, kv, 4, True, heads_per_item=2)
+
+
+def test_partition_defaults_to_one_head_per_item():
+    big = np.concatenate([[0], np.cumsum([4096] * 8)]).astype(np.int32)
+    _, info = _check_plan(big, big, 128, True)
+    assert info["heads_per_item"] == 1
+    _, info = _check_plan(big, big, 128, True, heads_per_item=8)
+    assert info["heads_per_item"] == 8
+
+
+def test_partition_rejects_a_head_block_that_does_not_divide():
+    import torch
+    p = mra.Plan(heads_per_item=3)
+    with pytest.raises(RuntimeError):
+        p.plan([0, 64], [0, 64], 4, True, torch.bfloat16)
+    lib = mra.lib()
+    assert lib.mla_plan_set_heads_per_item(p._h, -1) == 1
 
 
 def test_partition_balances_xcds_and_orders_heaviest_first():
     lens = [16, 32768, 40, 5000, 2000, 100, 8191, 3]
     qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    items, info = _check_plan(qo, qo, 16, True)
-    cost = np.where(items[:, 1] > 0, items[:, 6] + 64, 0).astype(np.int64)
-    per_xcd = [cost[x::8].sum() for x in range(8)]
-    group_cost = {}
-    for it, c in zip(items, cost):
-        if it[1] > 0:
-            group_cost[(it[7], it[2])] = group_cost.get((it[7], it[2]), 0) + c
-    assert max(per_xcd) - min(per_xcd) <= max(group_cost.values())
-    # inside one XCD queue the groups come heaviest first
-    for x in range(8):
-        seen = []
-        for it in items[x::8]:
-            if it[1] > 0 and (not seen or seen[-1] != (it[7], it[2])):
-                seen.append((it[7], it[2]))
-        costs = [group_cost[k] for k in seen]
-        assert costs == sorted(costs, reverse=True)
+    for hpi in (None, 4):
+        items, info = _check_plan(qo, qo, 16, True, heads_per_item=hpi)
+        cost = np.where(items[:, 1] > 0, (items[:, 7] + 64) * items[:, 3], 0).astype(np.int64)
+        per_xcd = [cost[x::8].sum() for x in range(8)]
+        group_cost = {}
+        for it, c in zip(items, cost):
+            if it[1] > 0:
+                key = _group(qo, it)
+                group_cost[key] = group_cost.get(key, 0) + c
+        assert max(per_xcd) - min(per_xcd) <= max(group_cost.values())
+        # inside one XCD queue the groups come heaviest first
+        for x in range(8):
+            seen = []
+            for it in items[x::8]:
+                if it[1] > 0 and (not seen or seen[-1] != _group(qo, it)):
+                    seen.append(_group(qo, it))
+            costs = [group_cost[k] for k in seen]
+            assert costs == sorted(costs, reverse=True)
 
 
 def test_partition_without_xcd_grouping_has_no_padding():

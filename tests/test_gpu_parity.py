@@ -135,6 +135,33 @@ def test_plan_run_matches_one_shot_and_repeats():
     assert torch.equal(o1, o3)
 
 
+HEAD_BLOCK_QO = [1, 31, 33, 64, 129, 300, 5, 0, 7, 260]
+HEAD_BLOCK_KV = [1, 31, 33, 64, 129, 300, 2, 9, 0, 700]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_head_blocks_match_the_oracle_and_single_heads(dtype, causal):
+    # items that run 2, 4 or 8 heads back to back, across short, tile-edge,
+    # empty and key-less sequences (the K/V ring runs on across heads)
+    x = workloads.ragged_inputs(HEAD_BLOCK_QO, HEAD_BLOCK_KV, 8, dtype, seed=39, causal=causal)
+    g = _to(x, DEV)
+    _flush(f"[gpu] head blocks dtype={dtype} causal={causal}")
+    ro, rl = oracle.prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale)
+    base = None
+    for hpi in (1, 2, 4, 8):
+        p = mra.Plan(heads_per_item=hpi).plan(x.qo_indptr, x.kv_indptr, 8, causal, dtype).upload()
+        assert p.info()["heads_per_item"] == hpi
+        o, lse = p.run(g.q, g.k, g.v, x.sm_scale)
+        torch.cuda.synchronize()
+        check(o, lse, ro, rl, dtype, f"head blocks of {hpi}")
+        # each head runs the same arithmetic whatever the block size
+        if base is None:
+            base = (o, lse)
+        else:
+            assert torch.equal(o, base[0]) and torch.equal(lse, base[1])
+
+
 def test_one_shot_on_two_streams():
     lens = [200, 90]
     x = _to(workloads.ragged_inputs(lens, lens, 2, torch.bfloat16, seed=38), DEV)
