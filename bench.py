@@ -94,7 +94,7 @@ def parse():
                     help="target CPU time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
-    ap.add_argument("--only", choices=["merge"], default=None,
+    ap.add_argument("--only", choices=["merge", "decompress"], default=None,
                     help="run only one secondary kernel (for profiling) and print its figures")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; "
@@ -247,7 +247,7 @@ def time_workload_prefill(mra, torch, x, steps, warmup, name):
             "flops": flops}
 
 
-def time_decompress(mra, torch, workloads, steps, warmup):
+def time_decompress(mra, torch, workloads, steps, warmup, with_prefill=True):
     d = workloads.decompress_batch(device="cuda")
     H = d.num_heads
     k, v = mra.decompress_kv(d.c_kv, d.k_rope, d.w_uk, d.w_uv, H)
@@ -263,13 +263,26 @@ def time_decompress(mra, torch, workloads, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     t = d.c_kv.shape[0]
     gemm_flops = 2.0 * 2 * t * 512 * H * 128
+    # algorithmic bytes: c_kv, k_rope and both weights read once, K and V written once
+    algo_bytes = 2.0 * (t * 512 + t * 64 + 2 * 512 * H * 128 + t * H * (192 + 128))
+    tflops = gemm_flops / ms / 1e9
+    out = {"workload": "decompress_batch: 8 x 4096 tokens, latent 512 -> 128 heads (K_nope, V), "
+                       "then causal prefill",
+           "decompress_ms": round(ms, 4), "decompress_TFLOP/s": round(tflops, 1),
+           "decompress_GB/s": round(algo_bytes / ms / 1e6, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                        "hbm_frac": round(algo_bytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                        "traffic": profile_traffic("decompress_kv_8x4096_128heads.txt",
+                                                   "mla_ragged_chunked_amd/csrc/decompress.hip"),
+                        "kernel": "decompress_kernel"}}
+    if not with_prefill:
+        return out
     x = workloads.PrefillInputs(d.q, k, v, d.indptr, d.indptr, H, True, d.sm_scale)
     pre = time_workload_prefill(mra, torch, x, steps, warmup, "prefill on the decompressed K/V")
-    return {"workload": "decompress_batch: 8 x 4096 tokens, latent 512 -> 128 heads (K_nope, V), "
-                        "then causal prefill",
-            "decompress_ms": round(ms, 4), "decompress_TFLOP/s": round(gemm_flops / ms / 1e9, 1),
-            "prefill_ms": pre["kernel_ms"], "prefill_TFLOP/s": pre["TFLOP/s"],
-            "end_to_end_ms": round(ms + pre["kernel_ms"], 4)}
+    out.update({"prefill_ms": pre["kernel_ms"], "prefill_TFLOP/s": pre["TFLOP/s"],
+                "end_to_end_ms": round(ms + pre["kernel_ms"], 4)})
+    return out
 
 
 def main():
@@ -295,6 +308,10 @@ def main():
     mra.lib()
     if args.only == "merge":
         print(json.dumps(time_merge(mra, torch, workloads, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "decompress":
+        print(json.dumps(time_decompress(mra, torch, workloads, args.steps, args.warmup,
+                                         with_prefill=False)), flush=True)
         return
     t0 = time.perf_counter()
     x = workloads.deepseek_v3_batch(device="cuda")

@@ -10,14 +10,26 @@
 //   V[t,h,:]       = c_kv[t,:] . W_UV[:, h*128 : h*128+128]
 // as two bf16 MFMA GEMMs ([T,512] x [512, H*128]) with fp32 accumulation.
 //
-// Tiling: one workgroup = one head x 256 tokens of either K or V (grid.z).
-// The product is computed transposed, C^T[n][t] = sum_c W[c][n] c_kv[t][c],
-// with v_mfma_f32_32x32x16_bf16: A = W^T (n rows, latent dims along k), B =
-// c_kv^T (token columns, latent dims along k). c_kv rows are k-contiguous
-// already; W is n-contiguous, so each 32-dim slice of W is transposed into
-// LDS while staging. Each accumulator lane then owns one token and groups of
-// four consecutive output dims, written as 8-byte stores. Four waves split
-// the 128 x 256 tile 2 x 2 (64 dims x 128 tokens each).
+// Design (MI355X):
+//  * One workgroup = 256 tokens x 2 heads (256 output dims) of either K or V
+//    (grid.z), 4 waves of 128 dims x 128 tokens, one wave per SIMD with its
+//    256 fp32 accumulators in AGPRs. Per MFMA a wave reads 512 B of LDS.
+//  * The product is computed transposed, C^T[n][t] = sum_c W[c][n] c_kv[t][c]
+//    with v_mfma_f32_32x32x16_bf16 (A = W^T, B = c_kv^T), so each accumulator
+//    lane owns one token and runs of four consecutive output dims, written
+//    as 8-byte stores (L2 merges them into whole lines).
+//  * Operands stream through a 4-stage LDS ring of 32-latent slices, loaded
+//    straight from HBM with global_load_lds_dwordx4 (no VGPR staging), one
+//    barrier per slice, three slices in flight. W keeps its natural layout
+//    (latent rows of 512 B with an XOR swizzle of the 16-byte chunks) and
+//    its A fragments are read with ds_read_b64_tr_b16; c_kv rows (64 B per
+//    slice) are swizzled so the B fragment reads are conflict free.
+//  * Measured on MI355X the kernel is bound by streaming the operands into
+//    LDS and by the output stores, not by the MFMAs (removing the MFMAs
+//    leaves the time unchanged); the output is 2.7 GB at the DeepSeek shape.
+//  * K workgroups also copy k_rope into dims 128..191 of both heads.
+//  * Tokens past the end load the last valid row and are not stored; an odd
+//    head count leaves the second half of the last pair idle.
 #include "internal.h"
 
 namespace mla {
@@ -25,154 +37,211 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
 constexpr int kTT = 256;                    // tokens per tile
-constexpr int kNT = 128;                    // output dims per tile (one head)
-constexpr int kKC = 32;                     // latent dims per stage
-constexpr int kWPitch = kKC * 2 + 16;       // bytes per W^T row in LDS
-constexpr int kCPitch = kKC * 2 + 16;       // bytes per c_kv row in LDS
-constexpr int kWBytes = kNT * kWPitch;
-constexpr int kCBytes = kTT * kCPitch;
-constexpr int kStage = kWBytes + kCBytes;
-constexpr int kWUnits = (kKC / 2) * (kNT / 8);        // (latent pair, 8-dim chunk)
-constexpr int kWPerThread = kWUnits / kThreads;       // 1
-constexpr int kCChunks = kTT * (kKC / 8);             // 16-byte chunks of c_kv
-constexpr int kCPerThread = kCChunks / kThreads;      // 4
-static_assert(kWUnits % kThreads == 0 && kCChunks % kThreads == 0, "staging split");
+constexpr int kHeads = 2;                   // heads per tile
+constexpr int kNT = kHeads * kDnope;        // 256 output dims per tile
+constexpr int kKC = 32;                     // latent dims per slice
+constexpr int kCBytes = kTT * kKC * 2;      // 16 KB: c_kv rows of 64 B
+constexpr int kWBytes = kKC * kNT * 2;      // 16 KB: W rows of 512 B
+constexpr int kStage = kCBytes + kWBytes;   // 32 KB
+constexpr int kStages = 4;
+constexpr int kSlices = kDlat / kKC;        // 16
+constexpr int kCLoads = kCBytes / 1024 / kWaves;   // 4 DMA blocks per wave
+constexpr int kWLoads = kWBytes / 1024 / kWaves;   // 4
+constexpr int kLoadsPerSlice = kCLoads + kWLoads;
+static_assert(kCLoads * kWaves * 1024 == kCBytes && kWLoads * kWaves * 1024 == kWBytes, "DMA split");
 
-__global__ __launch_bounds__(kThreads) void decompress_kernel(
-    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_rope,
-    const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv, int num_tokens,
-    int num_heads, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+// 16-byte chunk slot of c_kv chunk c (0..3) in token row t
+__device__ __forceinline__ int cslot(int t, int c) { return c ^ ((t >> 2) & 3); }
+// 16-byte chunk slot of W chunk c (0..31) in latent row r
+__device__ __forceinline__ int wslot(int r, int c) { return c ^ ((r & 3) << 2); }
+
+// One 16-byte-per-lane global -> LDS load (lane l's 16 bytes land at
+// lds_dst + 16 l), issued as inline asm so the compiler does not wait for
+// it before LDS reads; completion is awaited with wait_vmcnt before the
+// barrier that publishes a slice. Nothing else in this kernel uses M0.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds_dst) {
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    // each half as uint32_t before widening: readfirstlane returns int
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decompress_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_rope,
+                       const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv,
+                       int num_tokens, int num_heads, uint16_t* __restrict__ k_out,
+                       uint16_t* __restrict__ v_out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int t0 = blockIdx.x * kTT;
-    const int head = blockIdx.y;
+    const int head0 = blockIdx.y * kHeads;
     const bool is_v = blockIdx.z == 1;
     const uint16_t* w = is_v ? w_uv : w_uk;
     const int H = num_heads;
-    const int64_t wcols = (int64_t)H * kNT;
-    const int wn = wave & 1;     // dims  [64*wn, +64)
-    const int wt = wave >> 1;    // tokens [128*wt, +128)
+    // heads of this tile that exist (the second may not, for odd H)
+    const int n_heads = H - head0 < kHeads ? H - head0 : kHeads;
+    const int wn = wave & 1;     // head head0 + wn: dims [128 wn, +128) of the tile
+    const int wt = wave >> 1;    // tokens [128 wt, +128)
+    const bool wave_active = wn < n_heads;
 
-    u32x4_t wreg[kWPerThread][2];
-    u32x4_t creg[kCPerThread];
-
-    auto load_stage = [&](int c0) {
+    // ---- DMA addressing (per lane, per slice: base + 16-byte chunk) ----
+    // c_kv block j of this wave: tile rows 16 (4 wave + j) + lane/4, LDS slot
+    // lane%4 holds global chunk cslot(row, lane%4) of the slice.
+    uint32_t c_off[kCLoads];
 #pragma unroll
-        for (int j = 0; j < kWPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int p = u % (kKC / 2);
-            const int nc = u / (kKC / 2);
+    for (int j = 0; j < kCLoads; ++j) {
+        const int row = 16 * (kCLoads * wave + j) + (lane >> 2);
+        int t = t0 + row;
+        t = t < num_tokens ? t : num_tokens - 1;
+        c_off[j] = (uint32_t)(t - t0) * (kDlat * 2) + cslot(row, lane & 3) * 16;
+    }
+    // W block j of this wave: latent rows 2 (4 wave + j) + lane/32 of the
+    // slice, LDS slot lane%32 holds global chunk wslot(row, lane%32).
+    const int head_w1 = n_heads > 1 ? head0 + 1 : head0;   // clamp a missing head
+    uint32_t w_off[kWLoads];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-                wreg[j][h2] = *reinterpret_cast<const u32x4_t*>(
-                    w + (int64_t)(c0 + 2 * p + h2) * wcols + (int64_t)head * kNT + nc * 8);
-        }
+    for (int j = 0; j < kWLoads; ++j) {
+        const int row = 2 * (kWLoads * wave + j) + (lane >> 5);
+        const int c = wslot(row, lane & 31);                    // 0..31 over the 2 heads
+        const int hsel = c >= 16 ? head_w1 : head0;
+        w_off[j] = (uint32_t)row * (uint32_t)(H * kDnope * 2) + (uint32_t)(hsel * kDnope * 2) + (c & 15) * 16;
+    }
+    const uint8_t* cbase = reinterpret_cast<const uint8_t*>(c_kv + (int64_t)t0 * kDlat);
+    const uint8_t* wbase = reinterpret_cast<const uint8_t*>(w);
+    auto issue = [&](int slice) {
+        uint8_t* cs = smem + (slice % kStages) * kStage;
+        uint8_t* ws = cs + kCBytes;
+        const uint8_t* cb = cbase + slice * kKC * 2;
+        const uint8_t* wb = wbase + (int64_t)slice * kKC * H * kDnope * 2;
 #pragma unroll
-        for (int j = 0; j < kCPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int row = u / (kKC / 8);
-            const int c = u % (kKC / 8);
-            const int t = t0 + row;
-            creg[j] = t < num_tokens
-                          ? *reinterpret_cast<const u32x4_t*>(c_kv + (int64_t)t * kDlat + c0 + c * 8)
-                          : u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int j = 0; j < kCLoads; ++j) dma16(cb, c_off[j], cs + (kCLoads * wave + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < kWLoads; ++j) dma16(wb, w_off[j], ws + (kWLoads * wave + j) * 1024);
     };
 
-    auto store_stage = [&](int stage) {
-        uint8_t* ws = smem + stage * kStage;
-        uint8_t* cs = ws + kWBytes;
+    // ---- fragment addressing ----
+    // B (c_kv^T) fragment of token block tb, k-step ks: token row
+    // 128 wt + 32 tb + l32, chunk 2 ks + g.
+    int b_off[2];
 #pragma unroll
-        for (int j = 0; j < kWPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int p = u % (kKC / 2);
-            const int nc = u / (kKC / 2);
+    for (int ks = 0; ks < 2; ++ks) {
+        const int row = 128 * wt + l32;   // + 32 tb: (row >> 2) & 3 unchanged
+        b_off[ks] = row * (kKC * 2) + cslot(row, 2 * ks + g) * 16;
+    }
+    // A (W^T) fragment of dim block nb, k-step ks: two transposing reads.
+    // Lane (g, h = bit 4, r = bits 2-3, q = bits 0-1) supplies latent row
+    // 16 ks + 8 g + 4 t + r, dims 128 wn + 32 nb + 16 h + 4 q .. +4, and
+    // lane 16 h + j of each half receives dim 32 nb + 16 h + j with k-slots
+    // 8 g .. 8 g + 7 in natural latent order (as the c_kv fragments). The
+    // swizzle depends on row % 4 = r only, so (ks, t) are immediates.
+    int a_off[4];
+    {
+        const int tr_h = (lane >> 4) & 1;
+        const int tr_r = (lane & 15) >> 2;
+        const int tr_q = lane & 3;
+        const int row = 8 * g + tr_r;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w0 = wreg[j][0][e >> 1];
-                const uint32_t w1 = wreg[j][1][e >> 1];
-                const uint32_t packed = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                                : ((w0 & 0xffffu) | (w1 << 16));
-                *reinterpret_cast<uint32_t*>(ws + (nc * 8 + e) * kWPitch + 2 * p * 2) = packed;
-            }
+        for (int nb = 0; nb < 4; ++nb) {
+            const int chunk = (128 * wn + 32 * nb + 16 * tr_h + 4 * tr_q) / 8;
+            a_off[nb] = kCBytes + row * (kNT * 2) + wslot(row, chunk) * 16 + (tr_q & 1) * 8;
         }
+    }
+    auto afrag = [&](const uint8_t* st, int nb, int ks) {
+        bf16x8_t a;
 #pragma unroll
-        for (int j = 0; j < kCPerThread; ++j) {
-            const int u = tid + j * kThreads;
-            const int row = u / (kKC / 8);
-            const int c = u % (kKC / 8);
-            *reinterpret_cast<u32x4_t*>(cs + row * kCPitch + c * 16) = creg[j];
+        for (int t = 0; t < 2; ++t) {
+            const uint8_t* p = st + a_off[nb] + (16 * ks + 4 * t) * (kNT * 2);
+            const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+            const bf16x4_t y = __builtin_bit_cast(bf16x4_t, x);
+            a[4 * t + 0] = y[0];
+            a[4 * t + 1] = y[1];
+            a[4 * t + 2] = y[2];
+            a[4 * t + 3] = y[3];
         }
+        return a;
     };
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[4][4];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = f32x16_t{};
 
-    constexpr int kStages = kDlat / kKC;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int st = 0; st < kStages; ++st) {
-        const bool has_next = st + 1 < kStages;
-        if (has_next) load_stage((st + 1) * kKC);
-        const uint8_t* ws = smem + (st & 1) * kStage;
-        const uint8_t* cs = ws + kWBytes;
+    for (int s = 0; s < 3; ++s) issue(s);
+    for (int s = 0; s < kSlices; ++s) {
+        // slices issued: 0 .. min(s+2, last); slice s must be complete
+        if (s + 2 < kSlices) wait_vmcnt<2 * kLoadsPerSlice>();
+        else if (s + 1 < kSlices) wait_vmcnt<kLoadsPerSlice>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (s + 3 < kSlices) issue(s + 3);   // into slice s-1's stage, retired by the barrier
+        if (wave_active) {
+            const uint8_t* st = smem + (s % kStages) * kStage;
 #pragma unroll
-        for (int ks = 0; ks < kKC / 16; ++ks) {
-            bf16x8_t a[2], b[4];
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8_t a[4], b[4];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                a[nb] = *reinterpret_cast<const bf16x8_t*>(
-                    ws + (wn * 64 + nb * 32 + l32) * kWPitch + (ks * 16 + g * 8) * 2);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                b[tb] = *reinterpret_cast<const bf16x8_t*>(
-                    cs + (wt * 128 + tb * 32 + l32) * kCPitch + (ks * 16 + g * 8) * 2);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < 4; ++nb) a[nb] = afrag(st, nb, ks);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
-                    acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[tb], acc[nb][tb], 0, 0, 0);
-        }
-        if (has_next) store_stage((st + 1) & 1);
-        __syncthreads();
-    }
-
-    // epilogue: lane owns token t = tile col, dims in groups of 4
-    const int out_dim = is_v ? kDvo : kDqk;
-    uint16_t* dst_base = is_v ? v_out : k_out;
+                    b[tb] = *reinterpret_cast<const bf16x8_t*>(st + b_off[ks] + 32 * tb * (kKC * 2));
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int t = t0 + wt * 128 + tb * 32 + l32;
-        if (t >= num_tokens) continue;
-        uint16_t* dst = dst_base + ((int64_t)t * H + head) * out_dim;
+                for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const int n = wn * 64 + nb * 32 + grp * 8 + g * 4;
-                bf16x4_t o4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[nb][tb][grp * 4 + e];
-                *reinterpret_cast<bf16x4_t*>(dst + n) = o4;
+                    for (int tb = 0; tb < 4; ++tb)
+                        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[tb], acc[nb][tb], 0, 0, 0);
             }
         }
     }
 
-    // K workgroups also place k_rope after the NoPE part, for their tokens
+    // ---- epilogue: lane owns token 128 wt + 32 tb + l32, dims in runs of 4 ----
+    const int out_dim = is_v ? kDvo : kDqk;
+    uint16_t* dst_base = is_v ? v_out : k_out;
+    if (wave_active) {
+        const int head = head0 + wn;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int t = t0 + 128 * wt + 32 * tb + l32;
+            if (t < num_tokens) {
+                uint16_t* dst = dst_base + ((int64_t)t * H + head) * out_dim;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+                    for (int grp = 0; grp < 4; ++grp) {
+                        const int n = 32 * nb + 8 * grp + 4 * g;
+                        bf16x4_t o4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[nb][tb][4 * grp + e];
+                        *reinterpret_cast<bf16x4_t*>(dst + n) = o4;
+                    }
+                }
+            }
+        }
+    }
+    // K workgroups also place k_rope after the NoPE part of both heads
     if (!is_v) {
         constexpr int kChunksPerTok = kDrope * 2 / 16;   // 8
         for (int u = tid; u < kTT * kChunksPerTok; u += kThreads) {
@@ -181,7 +250,8 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
             const int t = t0 + row;
             if (t >= num_tokens) continue;
             const u32x4_t x = *reinterpret_cast<const u32x4_t*>(k_rope + (int64_t)t * kDrope + c * 8);
-            *reinterpret_cast<u32x4_t*>(k_out + ((int64_t)t * H + head) * kDqk + kDnope + c * 8) = x;
+            for (int hh = 0; hh < n_heads; ++hh)
+                *reinterpret_cast<u32x4_t*>(k_out + ((int64_t)t * H + head0 + hh) * kDqk + kDnope + c * 8) = x;
         }
     }
 }
@@ -193,8 +263,9 @@ hipError_t launch_decompress(const void* c_kv, const void* k_rope, const void* w
                              void* v_out, hipStream_t stream) {
     if (num_tokens <= 0) return hipSuccess;
     const int64_t tiles = (num_tokens + kTT - 1) / kTT;
-    if (tiles > 0x7fffffff || num_heads > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decompress_kernel, dim3((unsigned)tiles, (unsigned)num_heads, 2),
+    const int pairs = (num_heads + kHeads - 1) / kHeads;
+    if (tiles > 0x7fffffff || num_heads > 65535 || num_tokens > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(decompress_kernel, dim3((unsigned)tiles, (unsigned)pairs, 2),
                        dim3(kThreads), 0, stream, static_cast<const uint16_t*>(c_kv),
                        static_cast<const uint16_t*>(k_rope), static_cast<const uint16_t*>(w_uk),
                        static_cast<const uint16_t*>(w_uv), (int)num_tokens, num_heads,

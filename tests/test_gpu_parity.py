@@ -211,11 +211,15 @@ def test_merge_state_in_place():
 # decompression
 # ---------------------------------------------------------------------------
 
-def test_decompress_small_parity():
-    d = workloads.decompress_batch(num_seqs=2, seq_len=300, num_heads=3)
-    k, v = mra.decompress_kv(d.c_kv.to(DEV), d.k_rope.to(DEV), d.w_uk.to(DEV), d.w_uv.to(DEV), 3)
+@pytest.mark.parametrize("num_seqs,seq_len,num_heads", [(2, 300, 3), (1, 17, 1), (3, 129, 4)])
+def test_decompress_small_parity(num_seqs, seq_len, num_heads):
+    # ragged token tails (not multiples of the 256-token tile), odd head counts
+    d = workloads.decompress_batch(num_seqs=num_seqs, seq_len=seq_len, num_heads=num_heads)
+    _flush(f"[gpu] decompress T={num_seqs * seq_len} H={num_heads}")
+    k, v = mra.decompress_kv(d.c_kv.to(DEV), d.k_rope.to(DEV), d.w_uk.to(DEV), d.w_uv.to(DEV),
+                             num_heads)
     torch.cuda.synchronize()
-    rk, rv = oracle.decompress(d.c_kv, d.k_rope, d.w_uk, d.w_uv, 3)
+    rk, rv = oracle.decompress(d.c_kv, d.k_rope, d.w_uk, d.w_uv, num_heads)
     k, v = k.double().cpu(), v.double().cpu()
     # k_rope is copied, not computed
     assert torch.equal(k[:, :, 128:], rk[:, :, 128:])
@@ -309,7 +313,7 @@ def test_decompress_then_prefill_full_size():
     c_kv, k_rope = d.c_kv.cpu(), d.k_rope.cpu()
     rows = sample_rows(d.indptr, n_random=32, seed=5)
     idx = torch.tensor(rows)
-    for h in (3,):
+    for h in (3, H - 2):
         wk = d.w_uk[:, h * 128:(h + 1) * 128].contiguous().cpu()
         wv = d.w_uv[:, h * 128:(h + 1) * 128].contiguous().cpu()
         rk, rv = oracle.decompress(c_kv, k_rope, wk, wv, 1)           # fp64, all tokens
