@@ -247,6 +247,48 @@ def time_workload_prefill(mra, torch, x, steps, warmup, name):
             "flops": flops}
 
 
+def time_device_plan(mra, torch, x, steps, warmup):
+    """The same batch through the device-planned path (device indptrs, work
+    list built on the GPU, no host sync): eager, and replayed from a captured
+    graph. Times cover the planning kernels and the prefill."""
+    batch = len(x.qo_indptr) - 1
+    tq, tk = x.qo_indptr[-1], x.kv_indptr[-1]
+    dp = mra.DevicePlan(batch, tq, tk, x.num_heads, x.q.dtype)
+    qo_d = torch.tensor(x.qo_indptr, dtype=torch.int32, device="cuda")
+    kv_d = torch.tensor(x.kv_indptr, dtype=torch.int32, device="cuda")
+    out = torch.empty((tq, x.num_heads, 128), dtype=x.q.dtype, device="cuda")
+    lse = torch.empty((tq, x.num_heads), dtype=torch.float32, device="cuda")
+    run = lambda: dp.run(x.q, x.k, x.v, qo_d, kv_d, x.causal, x.sm_scale, out=out, lse=lse)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * x.num_heads * visible_pairs(x.qo_indptr, x.kv_indptr, x.causal) * 320
+    return {"workload": "deepseek_v3_batch through the device-planned path",
+            "eager_ms": round(eager_ms, 4), "eager_TFLOP/s": round(flops / eager_ms / 1e9, 1),
+            "graph_replay_ms": round(graph_ms, 4),
+            "graph_TFLOP/s": round(flops / graph_ms / 1e9, 1),
+            "invalid_flag": int(dp.invalid_flag().item())}
+
+
 def time_decompress(mra, torch, workloads, steps, warmup, with_prefill=True):
     d = workloads.decompress_batch(device="cuda")
     H = d.num_heads
@@ -361,6 +403,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline(oracle, torch, x, args.cpu_seconds)
     if not args.no_secondary:
         sec = {"merge_state": time_merge(mra, torch, workloads, args.steps, args.warmup)}
+        log("secondary: device-planned path ...")
+        sec["device_plan"] = time_device_plan(mra, torch, x, args.steps, args.warmup)
         del x
         torch.cuda.empty_cache()
         log("secondary: chunked prefill ...")

@@ -172,6 +172,42 @@ int mla_plan_set_xcds(mla_plan *plan, int32_t n_xcd);
 int mla_plan_set_heads_per_item(mla_plan *plan, int32_t heads_per_item);
 
 /*
+ * Device-planned prefill (for HIP graph capture and host-sync-free loops):
+ * the same operation as mla_ragged_prefill, but qo_indptr and kv_indptr are
+ * DEVICE int32 [batch+1] arrays read only by the GPU, and the work list is
+ * built on the GPU into a caller-provided workspace. The call enqueues three
+ * kernels (sequence order, work list, prefill) on `stream`, makes no
+ * synchronising call and allocates nothing, so it can be captured in a graph
+ * and replayed with new indptr contents (same batch and bounds).
+ *
+ *   batch        0 .. 4096 (0 is a no-op).
+ *   max_tq       upper bound on qo_indptr[batch]: q and out have at least
+ *                max_tq rows (and lse, if given). max_tk likewise bounds
+ *                kv_indptr[batch] and the rows of k and v. The grid size
+ *                depends only on batch, max_tq and num_heads.
+ *   workspace    device, 16-byte aligned, at least the size reported by
+ *                mla_device_plan_workspace_size(batch, max_tq, num_heads,
+ *                dtype); owned by the caller, reused across calls (calls on
+ *                one workspace must be ordered, e.g. on one stream).
+ *                Its first int32 is a flag the GPU sets nonzero when some
+ *                sequence's indptrs are invalid (not non-decreasing, negative,
+ *                beyond max_tq / max_tk, or indptr[0] != 0); such sequences
+ *                are skipped (no reads, their output rows are not written)
+ *                instead of faulting. Read it after the stream has run.
+ * Host-side arguments are validated as for mla_ragged_prefill before any
+ * HIP call. Outputs match mla_ragged_prefill bit for bit (every (row, head)
+ * is computed by the same arithmetic; only the order of work differs).
+ */
+int mla_device_plan_workspace_size(int32_t batch, int64_t max_tq, int32_t num_heads,
+                                   int32_t dtype, int64_t *bytes);
+int mla_ragged_prefill_device_plan(const void *q, const void *k, const void *v,
+                                   const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                   int32_t batch, int64_t max_tq, int64_t max_tk,
+                                   int32_t num_heads, int32_t causal, float sm_scale,
+                                   int32_t dtype, void *out, float *lse, void *workspace,
+                                   int64_t workspace_bytes, void *stream);
+
+/*
  * merge_state: combine two attention states computed over disjoint key sets
  * (the chunked-prefill combine of the causal new-token pass with the
  * non-causal context-chunk passes; the pages return each pass's (O, LSE)

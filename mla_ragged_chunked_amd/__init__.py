@@ -21,7 +21,7 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-__all__ = ["ragged_prefill", "merge_state", "decompress_kv", "Plan", "MlaError", "lib",
+__all__ = ["ragged_prefill", "merge_state", "decompress_kv", "Plan", "DevicePlan", "MlaError", "lib",
            "LIB_PATH", "DQK", "DVO", "EXPORTED_SYMBOLS"]
 
 DQK, DVO, DLAT, DROPE = 192, 128, 512, 64
@@ -34,7 +34,8 @@ EXPORTED_SYMBOLS = [
     "mla_status_string", "mla_last_error", "mla_version", "mla_ragged_prefill",
     "mla_plan_create", "mla_plan_destroy", "mla_ragged_plan", "mla_plan_upload",
     "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_set_xcds",
-    "mla_plan_set_heads_per_item",
+    "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
+    "mla_ragged_prefill_device_plan",
     "mla_merge_state", "mla_decompress_kv",
 ]
 
@@ -77,6 +78,9 @@ def lib():
         "mla_plan_items": ([P, P, I64], ctypes.c_int),
         "mla_plan_set_xcds": ([P, I32], ctypes.c_int),
         "mla_plan_set_heads_per_item": ([P, I32], ctypes.c_int),
+        "mla_device_plan_workspace_size": ([I32, I64, I32, I32, ctypes.POINTER(I64)], ctypes.c_int),
+        "mla_ragged_prefill_device_plan": ([P, P, P, P, P, I32, I64, I64, I32, I32, F, I32, P, P,
+                                            P, I64, P], ctypes.c_int),
         "mla_merge_state": ([P, P, P, P, P, P, I64, I32, I32, P], ctypes.c_int),
         "mla_decompress_kv": ([P, P, P, P, I64, I32, P, P, P], ctypes.c_int),
     }
@@ -184,6 +188,60 @@ class Plan:
                                             _ptr(lse) if return_lse else None,
                                             _stream(q.device)),
                    "mla_ragged_run")
+        return (out, lse) if return_lse else out
+
+
+class DevicePlan:
+    """Prefill whose work list is built on the GPU from device indptrs, into a
+    workspace this object owns: no host synchronisation and no allocation per
+    call, so `run` can be captured in a CUDA/HIP graph and replayed after the
+    indptr tensors' contents change (same batch, within max_tq / max_tk)."""
+
+    def __init__(self, batch: int, max_tq: int, max_tk: int, num_heads: int,
+                 dtype: torch.dtype = torch.bfloat16, device=None):
+        if dtype not in _DT:
+            raise ValueError("dtype must be torch.bfloat16 or torch.float32")
+        self._lib = lib()
+        nbytes = ctypes.c_int64()
+        _check(self._lib.mla_device_plan_workspace_size(int(batch), int(max_tq), int(num_heads),
+                                                        _DT[dtype], ctypes.byref(nbytes)),
+               "mla_device_plan_workspace_size")
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        self.workspace = torch.zeros(max(nbytes.value, 16), dtype=torch.uint8, device=dev)
+        self.batch, self.max_tq, self.max_tk = int(batch), int(max_tq), int(max_tk)
+        self.num_heads, self.dtype = int(num_heads), dtype
+
+    def invalid_flag(self) -> torch.Tensor:
+        """Device int32 flag: nonzero when some sequence's device indptrs were
+        invalid on the last run (those sequences were skipped)."""
+        return self.workspace[:4].view(torch.int32)
+
+    def run(self, q, k, v, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, causal: bool,
+            sm_scale: float, out=None, lse=None, return_lse: bool = True):
+        for t, name in ((q, "q"), (k, "k"), (v, "v"), (qo_indptr, "qo_indptr"),
+                        (kv_indptr, "kv_indptr")):
+            _dev_tensor(t, name)
+        if qo_indptr.dtype != torch.int32 or kv_indptr.dtype != torch.int32:
+            raise ValueError("device indptrs must be int32")
+        if qo_indptr.numel() != self.batch + 1 or kv_indptr.numel() != self.batch + 1:
+            raise ValueError("device indptrs must have batch + 1 entries")
+        if q.shape[0] < self.max_tq or k.shape[0] < self.max_tk:
+            raise ValueError("q must hold max_tq rows and k, v max_tk rows")
+        if q.shape[1] != self.num_heads or q.dtype != self.dtype:
+            raise ValueError("q does not match the plan's heads / dtype")
+        if out is None:
+            out = torch.empty((q.shape[0], self.num_heads, DVO), dtype=q.dtype, device=q.device)
+        if return_lse and lse is None:
+            lse = torch.empty((q.shape[0], self.num_heads), dtype=torch.float32, device=q.device)
+        _dev_tensor(out, "out")
+        _check_shapes(q, k, v, out, lse if return_lse else None)
+        with torch.cuda.device(q.device):
+            _check(self._lib.mla_ragged_prefill_device_plan(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(qo_indptr), _ptr(kv_indptr), self.batch,
+                self.max_tq, self.max_tk, self.num_heads, int(bool(causal)), float(sm_scale),
+                _DT[q.dtype], _ptr(out), _ptr(lse) if return_lse else None,
+                self.workspace.data_ptr(), self.workspace.numel(), _stream(q.device)),
+                "mla_ragged_prefill_device_plan")
         return (out, lse) if return_lse else out
 
 

@@ -367,6 +367,62 @@ int mla_ragged_prefill(const void* q, const void* k, const void* v, const int32_
     return do_run(p, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream));
 }
 
+int mla_device_plan_workspace_size(int32_t batch, int64_t max_tq, int32_t num_heads,
+                                   int32_t dtype, int64_t* bytes) {
+    if (bytes == nullptr) return fail(MLA_EINVAL, "bytes is NULL");
+    *bytes = 0;
+    if (int s = check_dtype(dtype)) return s;
+    if (batch < 0 || batch > mla::kDevicePlanMaxBatch)
+        return fail(MLA_EINVAL, "batch must be in [0, 4096] for device planning");
+    if (num_heads < 1 || num_heads > 65535) return fail(MLA_EINVAL, "num_heads must be in [1, 65535]");
+    if (max_tq < 0) return fail(MLA_EINVAL, "max_tq must be >= 0");
+    const int bm = dtype == MLA_DTYPE_BF16 ? mla::prefill_bf16_block_m() : mla::prefill_fp32_block_m();
+    const int64_t n = mla::device_plan_max_items(batch, max_tq, num_heads, bm);
+    *bytes = mla::device_plan_layout(batch, n).bytes;
+    return MLA_OK;
+}
+
+int mla_ragged_prefill_device_plan(const void* q, const void* k, const void* v,
+                                   const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                   int32_t batch, int64_t max_tq, int64_t max_tk,
+                                   int32_t num_heads, int32_t causal, float sm_scale,
+                                   int32_t dtype, void* out, float* lse, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
+    // validate everything before the first HIP call (the indptrs stay on the
+    // device and are checked there)
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_scale(sm_scale)) return s;
+    if (batch < 0 || batch > mla::kDevicePlanMaxBatch)
+        return fail(MLA_EINVAL, "batch must be in [0, 4096] for device planning");
+    if (num_heads < 1 || num_heads > 65535) return fail(MLA_EINVAL, "num_heads must be in [1, 65535]");
+    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
+    if (max_tq < 0 || max_tk < 0) return fail(MLA_EINVAL, "max_tq and max_tk must be >= 0");
+    if (max_tq * num_heads > INT32_MAX || max_tk * num_heads > INT32_MAX)
+        return fail(MLA_EUNSUPPORTED, "tokens x heads exceeds 2^31 rows");
+    if (batch == 0) return MLA_OK;
+    if (qo_indptr == nullptr || kv_indptr == nullptr) return fail(MLA_EINVAL, "indptr is NULL");
+    if (int s = check_tensors(q, k, v, out, lse, max_tq, max_tk)) return s;
+    if (workspace == nullptr || !aligned16(workspace))
+        return fail(MLA_EINVAL, "workspace must be non-NULL and 16-byte aligned");
+    const int bm = dtype == MLA_DTYPE_BF16 ? mla::prefill_bf16_block_m() : mla::prefill_fp32_block_m();
+    const int64_t n = mla::device_plan_max_items(batch, max_tq, num_heads, bm);
+    const mla::DevicePlanLayout l = mla::device_plan_layout(batch, n);
+    if (workspace_bytes < l.bytes)
+        return fail(MLA_EINVAL, "workspace is smaller than mla_device_plan_workspace_size");
+    if (n > INT32_MAX) return fail(MLA_EUNSUPPORTED, "too many work items");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = mla::launch_device_plan(qo_indptr, kv_indptr, batch, max_tq, max_tk, num_heads,
+                                           causal != 0, bm, workspace, n, s);
+    if (e != hipSuccess) return hip_fail(e, "device plan launch");
+    const WorkItem* items =
+        reinterpret_cast<const WorkItem*>(static_cast<const uint8_t*>(workspace) + l.items);
+    e = dtype == MLA_DTYPE_BF16
+            ? mla::launch_prefill_bf16(items, n, q, k, v, out, lse, num_heads, sm_scale, s)
+            : mla::launch_prefill_fp32(items, n, q, k, v, out, lse, num_heads, sm_scale, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return MLA_OK;
+}
+
 int mla_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                     void* o, float* lse, int64_t num_rows, int32_t head_dim, int32_t dtype,
                     void* stream) {

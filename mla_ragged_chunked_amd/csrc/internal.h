@@ -41,11 +41,24 @@ int prefill_fp32_block_m();
 // invalid input. `block_m` is the query-tile height, `n_xcd` the number of
 // XCDs work is grouped for (1 = no grouping).
 // `heads_per_item` is the head-block size (it must divide num_heads); 0
-// picks one: the largest of 8, 4, 2, 1 that divides num_heads and still
-// leaves at least kMinItemsPerSlot items for every workgroup slot.
+// means automatic (one head per item).
 bool build_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
                      int num_heads, bool causal, int block_m, int n_xcd, int heads_per_item,
                      std::vector<WorkItem>& out, std::string& err);
+
+// Device-side partitioner (device_plan.hip). The workspace holds, at these
+// byte offsets: a flag word (nonzero = some sequence had invalid indptrs and
+// was skipped), the sequence order, the tile prefix sums and the work list.
+constexpr int kDevicePlanMaxBatch = 4096;
+constexpr int kDevicePlanXcds = 8;
+struct DevicePlanLayout {
+    int64_t flag, order, prefix, items, bytes;
+};
+int64_t device_plan_max_items(int batch, int64_t max_tq, int num_heads, int block_m);
+DevicePlanLayout device_plan_layout(int batch, int64_t max_items);
+hipError_t launch_device_plan(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                              int64_t max_tq, int64_t max_tk, int num_heads, bool causal,
+                              int block_m, void* workspace, int64_t max_items, hipStream_t stream);
 
 // Kernel launchers (one kernel each, enqueued on `stream`).
 hipError_t launch_prefill_bf16(const WorkItem* items, int64_t n_items, const void* q,

@@ -223,3 +223,53 @@ def test_partition_without_xcd_grouping_has_no_padding():
     qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     items, info = _check_plan(qo, qo, 4, True, n_xcd=1)
     assert np.all(items[:, 1] > 0) and info["n_xcd"] == 1
+
+
+# ---------------------------------------------------------------------------
+# device-planned prefill: host-side checks (no HIP call is made)
+# ---------------------------------------------------------------------------
+
+def _ws_size(batch, max_tq, heads, dtype=0):
+    import ctypes
+    n = ctypes.c_int64(-1)
+    st = mra.lib().mla_device_plan_workspace_size(batch, max_tq, heads, dtype, ctypes.byref(n))
+    return st, n.value
+
+
+def test_device_plan_workspace_size():
+    st, a = _ws_size(16, 25729, 128)
+    assert st == 0 and a > 0
+    # the work list bound: 8 XCD bins x ceil(H/8) heads x (tiles of max_tq + one per sequence)
+    bm = 128
+    assert a >= 8 * 16 * (-(-25729 // bm) + 16) * 32
+    assert _ws_size(32, 25729, 128)[1] > a and _ws_size(16, 60000, 128)[1] > a
+    assert _ws_size(0, 0, 1)[0] == 0
+    assert _ws_size(4097, 100, 4)[0] == 1          # batch beyond the device sort
+    assert _ws_size(4, 100, 0)[0] == 1
+    assert _ws_size(4, 100, 4, dtype=7)[0] == 2
+
+
+def test_device_plan_rejects_invalid_arguments_before_any_hip_call():
+    l = mra.lib()
+    st, need = _ws_size(2, 64, 4)
+    args = [16, 16, 16, 16, 16, 2, 64, 64, 4, 1, 0.1, 0, 16, 16, 16, need, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["q", "k", "v", "qo", "kv", "batch", "max_tq", "max_tk", "heads", "causal",
+                 "scale", "dtype", "out", "lse", "ws", "ws_bytes", "stream"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return l.mla_ragged_prefill_device_plan(*a)
+
+    assert call(ws_bytes=need - 1) == 1                # workspace too small
+    assert call(ws=None) == 1
+    assert call(ws=8) == 1                             # misaligned workspace
+    assert call(scale=float("nan")) == 1
+    assert call(causal=2) == 1
+    assert call(batch=4097) == 1
+    assert call(qo=None) == 1
+    assert call(dtype=5) == 2
+    assert call(max_tq=-1) == 1
+    assert call(max_tq=(1 << 31) // 4 + 1) == 2        # tokens x heads beyond 2^31
+    assert call(batch=0) == 0                          # no-op

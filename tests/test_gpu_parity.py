@@ -162,6 +162,89 @@ def test_head_blocks_match_the_oracle_and_single_heads(dtype, causal):
             assert torch.equal(o, base[0]) and torch.equal(lse, base[1])
 
 
+DEVICE_PLAN_CASES = [
+    ([5, 300, 0, 7, 513, 1, 260], [2, 0, 9, 40, 513, 700, 33], 3),
+    ([1, 31, 33, 64, 129, 300], [1, 31, 33, 64, 129, 300], 16),
+    ([128] * 9, [1000] * 9, 8),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("case", range(len(DEVICE_PLAN_CASES)))
+def test_device_plan_matches_host_plan(dtype, causal, case):
+    qo_lens, kv_lens, heads = DEVICE_PLAN_CASES[case]
+    x = _to(workloads.ragged_inputs(qo_lens, kv_lens, heads, dtype, seed=40 + case, causal=causal),
+            DEV)
+    _flush(f"[gpu] device plan case {case} dtype={dtype} causal={causal}")
+    ref_o, ref_l = mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, causal, x.sm_scale)
+    tq, tk = x.qo_indptr[-1], x.kv_indptr[-1]
+    dp = mra.DevicePlan(len(qo_lens), tq, tk, heads, dtype)
+    qo_d = torch.tensor(x.qo_indptr, dtype=torch.int32, device=DEV)
+    kv_d = torch.tensor(x.kv_indptr, dtype=torch.int32, device=DEV)
+    o, l = dp.run(x.q, x.k, x.v, qo_d, kv_d, causal, x.sm_scale)
+    torch.cuda.synchronize()
+    assert int(dp.invalid_flag().item()) == 0
+    # same arithmetic per (row, head); only the order of work differs
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_device_plan_flags_invalid_indptrs_and_skips_them():
+    lens = [40, 70, 90]
+    x = _to(workloads.ragged_inputs(lens, lens, 4, torch.bfloat16, seed=43), DEV)
+    tq = x.qo_indptr[-1]
+    dp = mra.DevicePlan(3, tq, tq, 4)
+    # sequence 1 ends beyond max_tq: skipped; sequences 0 and 2 stay in bounds
+    bad = [0, 40, tq + 500, tq]
+    assert all(0 <= a <= tq for a in (bad[0], bad[1], bad[3]))
+    qo_d = torch.tensor(bad, dtype=torch.int32, device=DEV)
+    out = torch.zeros((tq, 4, 128), dtype=torch.bfloat16, device=DEV)
+    o, l = dp.run(x.q, x.k, x.v, qo_d, qo_d, True, x.sm_scale, out=out)
+    torch.cuda.synchronize()
+    assert int(dp.invalid_flag().item()) != 0
+    ref_o, ref_l = mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    assert torch.equal(o[:40], ref_o[:40]) and torch.equal(l[:40], ref_l[:40])
+
+
+def test_device_plan_in_a_captured_graph_follows_new_indptrs():
+    # one captured graph (device plan + prefill), replayed after the indptr
+    # contents change; every replay is checked against the eager host path
+    heads, batch, max_t = 4, 4, 1024
+    g = torch.Generator().manual_seed(44)
+    q = workloads.randn((max_t, heads, 192), g, torch.bfloat16, "cpu").to(DEV)
+    k = workloads.randn((max_t, heads, 192), g, torch.bfloat16, "cpu").to(DEV)
+    v = workloads.randn((max_t, heads, 128), g, torch.bfloat16, "cpu").to(DEV)
+    scale = 192 ** -0.5
+    qo_d = torch.zeros(batch + 1, dtype=torch.int32, device=DEV)
+    kv_d = torch.zeros(batch + 1, dtype=torch.int32, device=DEV)
+    out = torch.zeros((max_t, heads, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros((max_t, heads), dtype=torch.float32, device=DEV)
+    dp = mra.DevicePlan(batch, max_t, max_t, heads)
+    first = workloads.indptr_from_lengths([100, 200, 300, 400])
+    qo_d.copy_(torch.tensor(first, dtype=torch.int32))
+    kv_d.copy_(torch.tensor(first, dtype=torch.int32))
+    dp.run(q, k, v, qo_d, kv_d, True, scale, out=out, lse=lse)      # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dp.run(q, k, v, qo_d, kv_d, True, scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for lens in ([100, 200, 300, 400], [1, 513, 0, 300], [256, 256, 256, 256], [17, 4, 900, 33]):
+        ind = workloads.indptr_from_lengths(lens)
+        qo_d.copy_(torch.tensor(ind, dtype=torch.int32))
+        kv_d.copy_(torch.tensor(ind, dtype=torch.int32))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t = ind[-1]
+        ref_o, ref_l = mra.ragged_prefill(q[:t].contiguous(), k[:t].contiguous(), v[:t].contiguous(),
+                                          ind, ind, True, scale)
+        torch.cuda.synchronize()
+        _flush(f"[gpu] graph replay lens={lens}")
+        assert torch.equal(out[:t], ref_o) and torch.equal(lse[:t], ref_l)
+        assert int(dp.invalid_flag().item()) == 0
+
+
 def test_one_shot_on_two_streams():
     lens = [200, 90]
     x = _to(workloads.ragged_inputs(lens, lens, 2, torch.bfloat16, seed=38), DEV)
