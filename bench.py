@@ -228,6 +228,49 @@ def time_chunked(mra, torch, workloads, steps, warmup):
             "flops_per_step": flops}
 
 
+def time_paged_context(mra, torch, workloads, steps, warmup, page=64):
+    """One chunked-prefill context pass (8 x 2048 new tokens against 8 x 4096
+    context keys, non-causal) with the context in a page pool in random page
+    order, next to the same pass on contiguous K/V. Both through the one-shot
+    calls (each includes its host planning)."""
+    c = workloads.chunked_prefill(device="cuda")
+    ch = c.chunks[0]
+    tk, heads = ch.k.shape[0], ch.num_heads
+    n_pages = tk // page
+    g = torch.Generator(device="cuda").manual_seed(3)
+    perm = torch.randperm(n_pages, generator=g, device="cuda")
+    kc = torch.empty((n_pages, page, heads, 192), dtype=ch.k.dtype, device="cuda")
+    vc = torch.empty((n_pages, page, heads, 128), dtype=ch.v.dtype, device="cuda")
+    kc.index_copy_(0, perm, ch.k.view(n_pages, page, heads, 192))
+    vc.index_copy_(0, perm, ch.v.view(n_pages, page, heads, 128))
+    lens = [b - a for a, b in zip(ch.kv_indptr, ch.kv_indptr[1:])]
+    per = max(n // page for n in lens)
+    table = perm.view(len(lens), per).to(torch.int32).contiguous()
+    out = torch.empty((ch.q.shape[0], heads, 128), dtype=ch.q.dtype, device="cuda")
+    lse = torch.empty((ch.q.shape[0], heads), dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+    contig = timed(lambda: mra.ragged_prefill(ch.q, ch.k, ch.v, ch.qo_indptr, ch.kv_indptr, False,
+                                              ch.sm_scale, out=out, lse=lse))
+    paged = timed(lambda: mra.ragged_prefill_paged(ch.q, kc, vc, ch.qo_indptr, ch.kv_indptr,
+                                                   table, False, ch.sm_scale, out=out, lse=lse))
+    flops = 2.0 * heads * visible_pairs(ch.qo_indptr, ch.kv_indptr, False) * 320
+    return {"workload": f"context pass 8 x (2048 queries x 4096 keys), 128 heads, pages of {page} "
+                        "in random order",
+            "contiguous_ms": round(contig, 4), "paged_ms": round(paged, 4),
+            "contiguous_TFLOP/s": round(flops / contig / 1e9, 1),
+            "paged_TFLOP/s": round(flops / paged / 1e9, 1)}
+
+
 def time_workload_prefill(mra, torch, x, steps, warmup, name):
     plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, x.num_heads, x.causal).upload()
     out = torch.empty((x.q.shape[0], x.num_heads, 128), dtype=x.q.dtype, device="cuda")
@@ -409,6 +452,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: chunked prefill ...")
         sec["chunked_prefill"] = time_chunked(mra, torch, workloads, max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
+        log("secondary: paged context pass ...")
+        sec["paged_context"] = time_paged_context(mra, torch, workloads, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
         log("secondary: skewed batch ...")
         xs = workloads.skewed_batch(device="cuda")

@@ -103,6 +103,34 @@ int mla_ragged_prefill(const void *q, const void *k, const void *v,
                        int32_t dtype, void *out, float *lse, void *stream);
 
 /*
+ * Paged K/V variant of mla_ragged_prefill: the keys and values come from
+ * page-organised caches through a block table instead of contiguous [Tk, H, D]
+ * buffers (how serving systems hold a request's prefix: the page pool and
+ * block table of "[DeepseekR1] How ragged prefill manage kv_cache?", sglang
+ * issue 3849, token_to_kv_pool; and the block_table / slot_mapping of
+ * "[KVCache] PagedKVCache refactor, FlashInfer JIT and MLA integration").
+ *
+ *   k_cache      device [num_pages, page_size, H, 192], dtype `dtype`.
+ *   v_cache      device [num_pages, page_size, H, 128].
+ *   block_table  DEVICE int32 [batch, max_pages]: key j of sequence b is slot
+ *                j % page_size of page block_table[b * max_pages + j / page_size].
+ *                Entries outside [0, num_pages) are clamped into the cache
+ *                (no out-of-bounds access; the result is then meaningless).
+ *   page_size    a positive multiple of 32.
+ *   kv_indptr    HOST, as for mla_ragged_prefill: only the lengths
+ *                kv_indptr[b+1] - kv_indptr[b] are used (each must be at most
+ *                max_pages * page_size).
+ * Everything else (q, out, lse, qo_indptr, causal, sm_scale, dtype, stream)
+ * is as for mla_ragged_prefill; for the same keys and values the outputs are
+ * identical bit for bit to the contiguous call.
+ */
+int mla_ragged_prefill_paged(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *qo_indptr, const int32_t *kv_indptr,
+                             const int32_t *block_table, int32_t max_pages, int32_t page_size,
+                             int32_t num_pages, int32_t batch, int32_t num_heads, int32_t causal,
+                             float sm_scale, int32_t dtype, void *out, float *lse, void *stream);
+
+/*
  * Plan / run split (the pages plan once per batch and run once per layer:
  * "vllm.v1.attention.backends.mla.prefill.flashinfer", plan() inside
  * finalize_attention_metadata versus run() inside run_prefill_new_tokens).

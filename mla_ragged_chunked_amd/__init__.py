@@ -21,7 +21,7 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-__all__ = ["ragged_prefill", "merge_state", "decompress_kv", "Plan", "DevicePlan", "MlaError", "lib",
+__all__ = ["ragged_prefill", "ragged_prefill_paged", "merge_state", "decompress_kv", "Plan", "DevicePlan", "MlaError", "lib",
            "LIB_PATH", "DQK", "DVO", "EXPORTED_SYMBOLS"]
 
 DQK, DVO, DLAT, DROPE = 192, 128, 512, 64
@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = [
     "mla_plan_create", "mla_plan_destroy", "mla_ragged_plan", "mla_plan_upload",
     "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_set_xcds",
     "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
-    "mla_ragged_prefill_device_plan",
+    "mla_ragged_prefill_device_plan", "mla_ragged_prefill_paged",
     "mla_merge_state", "mla_decompress_kv",
 ]
 
@@ -81,6 +81,8 @@ def lib():
         "mla_device_plan_workspace_size": ([I32, I64, I32, I32, ctypes.POINTER(I64)], ctypes.c_int),
         "mla_ragged_prefill_device_plan": ([P, P, P, P, P, I32, I64, I64, I32, I32, F, I32, P, P,
                                             P, I64, P], ctypes.c_int),
+        "mla_ragged_prefill_paged": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, I32, P,
+                                      P, P], ctypes.c_int),
         "mla_merge_state": ([P, P, P, P, P, P, I64, I32, I32, P], ctypes.c_int),
         "mla_decompress_kv": ([P, P, P, P, I64, I32, P, P, P], ctypes.c_int),
     }
@@ -290,6 +292,45 @@ def ragged_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qo_indptr,
                                     _DT[q.dtype], _ptr(out), _ptr(lse) if return_lse else None,
                                     _stream(q.device)),
                "mla_ragged_prefill")
+    return (out, lse) if return_lse else out
+
+
+def ragged_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         qo_indptr, kv_indptr, block_table: torch.Tensor, causal: bool,
+                         sm_scale: float, return_lse: bool = True,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Ragged MLA prefill over paged K/V. k_cache [P, page, H, 192] and
+    v_cache [P, page, H, 128] on the GPU, block_table int32 [batch, max_pages]
+    on the GPU, host indptrs (kv_indptr gives the context lengths)."""
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                    (block_table, "block_table")):
+        _dev_tensor(t, name)
+    qo, kv = _indptr(qo_indptr), _indptr(kv_indptr)
+    if len(qo) != len(kv) or len(qo) < 1:
+        raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+    if qo[-1] != q.shape[0]:
+        raise ValueError("qo_indptr total does not match the token count of q")
+    if k_cache.dim() != 4 or v_cache.dim() != 4 or k_cache.shape[:3] != v_cache.shape[:3]:
+        raise ValueError("caches must be [pages, page_size, heads, dim] with matching pages")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+            block_table.shape[0] != len(qo) - 1:
+        raise ValueError("block_table must be int32 [batch, max_pages]")
+    n_pages, page, heads = k_cache.shape[:3]
+    tq = q.shape[0]
+    if out is None:
+        out = torch.empty((tq, heads, DVO), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((tq, heads), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, "out")
+    _check_shapes(q, k_cache.view(-1, heads, k_cache.shape[3]),
+                  v_cache.view(-1, heads, v_cache.shape[3]), out, lse if return_lse else None)
+    with torch.cuda.device(q.device):
+        _check(lib().mla_ragged_prefill_paged(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), qo.ctypes.data, kv.ctypes.data,
+            _ptr(block_table), block_table.shape[1], page, n_pages, len(qo) - 1, heads,
+            int(bool(causal)), float(sm_scale), _DT[q.dtype], _ptr(out),
+            _ptr(lse) if return_lse else None, _stream(q.device)),
+            "mla_ragged_prefill_paged")
     return (out, lse) if return_lse else out
 
 

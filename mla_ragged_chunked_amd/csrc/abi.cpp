@@ -133,6 +133,7 @@ struct mla_plan {
     int32_t batch = 0, num_heads = 0, causal = 0, dtype = -1, block_m = 0;
     int32_t n_xcd = 8;
     int32_t heads_per_item = 0;   // 0 = chosen by the planner
+    bool paged = false;           // items carry the sequence index in kv_start
     bool planned = false;
     bool uploaded = false;
     DeviceWorkList dwl;
@@ -166,7 +167,7 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out,
 }
 
 int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, int32_t heads,
-            int32_t causal, int32_t dtype) {
+            int32_t causal, int32_t dtype, bool paged = false) {
     if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
     p->planned = false;
     p->uploaded = false;
@@ -179,7 +180,7 @@ int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, in
     std::string err;
     try {
         if (!mla::build_work_list(qo, kv, batch, heads, causal != 0, bm, p->n_xcd,
-                                  p->heads_per_item, p->items, err))
+                                  p->heads_per_item, p->items, err, paged))
             return fail(MLA_EINVAL, err);
     } catch (const std::bad_alloc&) {
         return fail(MLA_ENOMEM, "host allocation of the work list failed");
@@ -196,18 +197,22 @@ int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, in
     p->causal = causal;
     p->dtype = dtype;
     p->block_m = bm;
+    p->paged = paged;
     p->planned = true;
     return MLA_OK;
 }
 
 int do_run(const mla_plan* p, const void* q, const void* k, const void* v, float sm_scale,
-           int32_t dtype, void* out, float* lse, hipStream_t stream) {
+           int32_t dtype, void* out, float* lse, hipStream_t stream,
+           const mla::PagedKv* paged = nullptr) {
     if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (p->paged != (paged != nullptr))
+        return fail(MLA_ESTATE, "plan and call disagree on paged K/V");
     if (!p->planned) return fail(MLA_ESTATE, "plan has not been built");
     if (!p->uploaded) return fail(MLA_ESTATE, "plan has not been uploaded (mla_plan_upload)");
     if (dtype != p->dtype) return fail(MLA_ESTATE, "dtype differs from the planned dtype");
     if (int s = check_scale(sm_scale)) return s;
-    if (int s = check_tensors(q, k, v, out, lse, p->tq, p->tk)) return s;
+    if (int s = check_tensors(q, k, v, out, lse, p->tq, paged != nullptr ? 1 : p->tk)) return s;
     int cur = -1;
     hipError_t e = hipGetDevice(&cur);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -215,8 +220,10 @@ int do_run(const mla_plan* p, const void* q, const void* k, const void* v, float
     if (p->items.empty()) return MLA_OK;
     const int64_t n = static_cast<int64_t>(p->items.size());
     e = dtype == MLA_DTYPE_BF16
-            ? mla::launch_prefill_bf16(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale, stream)
-            : mla::launch_prefill_fp32(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale, stream);
+            ? mla::launch_prefill_bf16(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale,
+                                       stream, paged)
+            : mla::launch_prefill_fp32(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale,
+                                       stream, paged);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     return MLA_OK;
 }
@@ -224,6 +231,64 @@ int do_run(const mla_plan* p, const void* q, const void* k, const void* v, float
 // One-shot calls keep one plan per (device, stream).
 std::mutex g_oneshot_mu;
 std::map<std::pair<int, void*>, mla_plan*>* g_oneshot = nullptr;
+
+// One-shot prefill (plan + upload + run) with a plan kept per (device, stream).
+int oneshot(const void* q, const void* k, const void* v, const int32_t* qo_indptr,
+            const int32_t* kv_indptr, int32_t batch, int32_t num_heads, int32_t causal,
+            float sm_scale, int32_t dtype, void* out, float* lse, void* stream,
+            const mla::PagedKv* paged) {
+    // validate everything before the first HIP call
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_scale(sm_scale)) return s;
+    if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
+    if (num_heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
+    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
+    if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
+        return fail(MLA_EINVAL, "indptr is NULL");
+    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
+    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
+    if (int s = check_tensors(q, k, v, out, lse, tq, paged != nullptr ? 1 : tk)) return s;
+    mla_plan scratch_check;
+    if (int s = do_plan(&scratch_check, qo_indptr, kv_indptr, batch, num_heads, causal, dtype,
+                        paged != nullptr))
+        return s;
+    if (scratch_check.items.empty()) return MLA_OK;
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    mla_plan* p = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_oneshot_mu);
+        if (g_oneshot == nullptr) g_oneshot = new (std::nothrow) std::map<std::pair<int, void*>, mla_plan*>();
+        if (g_oneshot == nullptr) return fail(MLA_ENOMEM, "one-shot plan table");
+        auto key = std::make_pair(dev, stream);
+        auto it = g_oneshot->find(key);
+        if (it == g_oneshot->end()) {
+            p = new (std::nothrow) mla_plan();
+            if (p == nullptr) return fail(MLA_ENOMEM, "one-shot plan");
+            (*g_oneshot)[key] = p;
+        } else {
+            p = it->second;
+        }
+    }
+    // Calls on one stream are serialised by the caller's stream order; the
+    // host-side plan object is per (device, stream), so a thread per stream
+    // never shares it.
+    p->items.swap(scratch_check.items);
+    p->tq = scratch_check.tq;
+    p->tk = scratch_check.tk;
+    p->batch = batch;
+    p->num_heads = num_heads;
+    p->causal = causal;
+    p->dtype = dtype;
+    p->block_m = scratch_check.block_m;
+    p->paged = scratch_check.paged;
+    p->planned = true;
+    p->uploaded = false;
+    if (int s = mla_plan_upload(p, stream)) return s;
+    return do_run(p, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream), paged);
+}
 
 }  // namespace
 
@@ -316,55 +381,33 @@ int mla_ragged_prefill(const void* q, const void* k, const void* v, const int32_
                        const int32_t* kv_indptr, int32_t batch, int32_t num_heads,
                        int32_t causal, float sm_scale, int32_t dtype, void* out, float* lse,
                        void* stream) {
-    // validate everything before the first HIP call
-    if (int s = check_dtype(dtype)) return s;
-    if (int s = check_scale(sm_scale)) return s;
-    if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
-    if (num_heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
-    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
-    if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
-        return fail(MLA_EINVAL, "indptr is NULL");
-    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
-    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
-    if (int s = check_tensors(q, k, v, out, lse, tq, tk)) return s;
-    mla_plan scratch_check;
-    if (int s = do_plan(&scratch_check, qo_indptr, kv_indptr, batch, num_heads, causal, dtype))
-        return s;
-    if (scratch_check.items.empty()) return MLA_OK;
+    return oneshot(q, k, v, qo_indptr, kv_indptr, batch, num_heads, causal, sm_scale, dtype, out,
+                   lse, stream, nullptr);
+}
 
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    mla_plan* p = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_oneshot_mu);
-        if (g_oneshot == nullptr) g_oneshot = new (std::nothrow) std::map<std::pair<int, void*>, mla_plan*>();
-        if (g_oneshot == nullptr) return fail(MLA_ENOMEM, "one-shot plan table");
-        auto key = std::make_pair(dev, stream);
-        auto it = g_oneshot->find(key);
-        if (it == g_oneshot->end()) {
-            p = new (std::nothrow) mla_plan();
-            if (p == nullptr) return fail(MLA_ENOMEM, "one-shot plan");
-            (*g_oneshot)[key] = p;
-        } else {
-            p = it->second;
+int mla_ragged_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                             int32_t num_pages, int32_t batch, int32_t num_heads, int32_t causal,
+                             float sm_scale, int32_t dtype, void* out, float* lse, void* stream) {
+    if (page_size < 32 || page_size % 32 != 0)
+        return fail(MLA_EINVAL, "page_size must be a positive multiple of 32");
+    if (max_pages < 1 || num_pages < 1) return fail(MLA_EINVAL, "max_pages and num_pages must be >= 1");
+    if ((int64_t)num_pages * page_size * (int64_t)(num_heads > 0 ? num_heads : 1) > INT32_MAX)
+        return fail(MLA_EUNSUPPORTED, "cache tokens x heads exceeds 2^31 rows");
+    if (batch > 0 && (block_table == nullptr ||
+                      (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))
+        return fail(MLA_EINVAL, "block_table must be non-NULL and 4-byte aligned");
+    if (batch > 0 && kv_indptr != nullptr) {
+        for (int32_t b = 0; b < batch; ++b) {
+            const int64_t len = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+            if (len > (int64_t)max_pages * page_size)
+                return fail(MLA_EINVAL, "a sequence's context exceeds max_pages x page_size");
         }
     }
-    // Calls on one stream are serialised by the caller's stream order; the
-    // host-side plan object is per (device, stream), so a thread per stream
-    // never shares it.
-    p->items.swap(scratch_check.items);
-    p->tq = scratch_check.tq;
-    p->tk = scratch_check.tk;
-    p->batch = batch;
-    p->num_heads = num_heads;
-    p->causal = causal;
-    p->dtype = dtype;
-    p->block_m = scratch_check.block_m;
-    p->planned = true;
-    p->uploaded = false;
-    if (int s = mla_plan_upload(p, stream)) return s;
-    return do_run(p, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream));
+    const mla::PagedKv pg{block_table, max_pages, page_size, num_pages};
+    return oneshot(q, k_cache, v_cache, qo_indptr, kv_indptr, batch, num_heads, causal, sm_scale,
+                   dtype, out, lse, stream, &pg);
 }
 
 int mla_device_plan_workspace_size(int32_t batch, int64_t max_tq, int32_t num_heads,

@@ -32,6 +32,18 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
 
+// Paged K/V source. The caches are [num_pages, page_size, H, D]; key j of
+// sequence b sits in page block_table[b * max_pages + j / page_size], slot
+// j % page_size. page_size is a multiple of 32, so a 32-key tile lies in one
+// page. In paged mode WorkItem::kv_start holds the sequence index b. Page
+// indices read from the (device) table are clamped to [0, num_pages).
+struct PagedKv {
+    const int32_t* block_table;  // device int32 [batch, max_pages]
+    int32_t max_pages;
+    int32_t page_size;
+    int32_t num_pages;
+};
+
 // Query-tile heights of the two prefill kernels (each kernel file owns its
 // tile shape; the planner asks for it).
 int prefill_bf16_block_m();
@@ -42,9 +54,10 @@ int prefill_fp32_block_m();
 // XCDs work is grouped for (1 = no grouping).
 // `heads_per_item` is the head-block size (it must divide num_heads); 0
 // means automatic (one head per item).
+// `kv_start_is_seq` stores the sequence index in kv_start (paged K/V).
 bool build_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
                      int num_heads, bool causal, int block_m, int n_xcd, int heads_per_item,
-                     std::vector<WorkItem>& out, std::string& err);
+                     std::vector<WorkItem>& out, std::string& err, bool kv_start_is_seq = false);
 
 // Device-side partitioner (device_plan.hip). The workspace holds, at these
 // byte offsets: a flag word (nonzero = some sequence had invalid indptrs and
@@ -61,12 +74,15 @@ hipError_t launch_device_plan(const int32_t* qo_indptr, const int32_t* kv_indptr
                               int block_m, void* workspace, int64_t max_items, hipStream_t stream);
 
 // Kernel launchers (one kernel each, enqueued on `stream`).
+// `paged` == nullptr: contiguous K/V ([Tk, H, D], rows from kv_start).
 hipError_t launch_prefill_bf16(const WorkItem* items, int64_t n_items, const void* q,
                                const void* k, const void* v, void* out, float* lse,
-                               int num_heads, float sm_scale, hipStream_t stream);
+                               int num_heads, float sm_scale, hipStream_t stream,
+                               const PagedKv* paged = nullptr);
 hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const void* q,
                                const void* k, const void* v, void* out, float* lse,
-                               int num_heads, float sm_scale, hipStream_t stream);
+                               int num_heads, float sm_scale, hipStream_t stream,
+                               const PagedKv* paged = nullptr);
 hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b,
                         const float* lse_b, void* o, float* lse, int64_t num_rows,
                         int dtype_bf16, hipStream_t stream);

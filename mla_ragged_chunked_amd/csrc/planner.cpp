@@ -41,7 +41,7 @@ struct Tile {
 
 bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_heads,
                      bool causal, int block_m, int n_xcd, int heads_per_item,
-                     std::vector<WorkItem>& out, std::string& err) {
+                     std::vector<WorkItem>& out, std::string& err, bool kv_start_is_seq) {
     out.clear();
     if (batch < 0) { err = "batch must be >= 0"; return false; }
     if (num_heads < 1 || num_heads > 65535) { err = "num_heads must be in [1, 65535]"; return false; }
@@ -70,7 +70,7 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
             Tile t;
             t.q_row0 = qo[b] + r0;
             t.n_rows = std::min(block_m, qo_len - r0);
-            t.kv_start = kv[b];
+            t.kv_start = kv_start_is_seq ? b : kv[b];
             t.kv_len = kv_len;
             // row r sees keys < kv_len - qo_len + (r0 + r) + 1 when causal
             t.diag0 = causal ? kv_len - qo_len + r0 : kv_len;

@@ -124,11 +124,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
                          const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                          uint16_t* __restrict__ out, float* __restrict__ lse, int num_heads,
-                         float scale_log2) {
+                         float scale_log2, PagedKv pg,
+                         const int32_t* __restrict__ block_table) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
     const WorkItem it = items[blockIdx.x];
@@ -171,7 +173,9 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     // V: 8 blocks of 4 rows x 256 B; row r's chunk c sits at slot vslot(r, c).
     // Keys at or past kv_len load the last valid row instead (finite data;
     // the mask gives those keys p = 0).
-    const int64_t kv_row0 = (int64_t)it.kv_start * H;   // row index of key 0, head 0
+    // row index of key 0, head 0 (contiguous K/V; paged K/V address each tile
+    // through its page)
+    const int64_t kv_row0 = kPaged ? 0 : (int64_t)it.kv_start * H;
     const int last_key = it.kv_len - 1;
     // Per-lane byte offsets (from the tile's first key row) of this wave's
     // loads: 3 K blocks and 2 V blocks; recomputed with the clamp only on a
@@ -200,13 +204,25 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         ld_off[j] = (uint32_t)ld_row[j] * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
     const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k + kv_row0 * kDqk);
     const uint8_t* vseq = reinterpret_cast<const uint8_t*>(v + kv_row0 * kDvo);
-    // Tile kt of head `head` into `stage`.
-    auto issue_tile = [&](int head, int kt, int stage) {
+    // Table entry of key tile kt (paged K/V). The block table is a kernel
+    // argument of its own, __restrict__, so this is a scalar load, which does
+    // not count against the DMA waits; the raw value is clamped only where it
+    // is used, an issue later, so the load's latency is never waited for.
+    auto page_entry = [&](int kt) {
+        return block_table[(int64_t)it.kv_start * pg.max_pages + (kt * kBN) / pg.page_size];
+    };
+    // Tile kt of head `head` into `stage` (`entry`: its table entry, paged K/V only).
+    auto issue_tile = [&](int head, int kt, int stage, int entry) {
         uint8_t* ks = smem + stage * kStage;
         uint8_t* vs = ks + kKBytes;
         const int key0 = kt * kBN;
-        const uint8_t* kb = kseq + ((uint64_t)key0 * H + head) * (kDqk * 2);
-        const uint8_t* vb = vseq + ((uint64_t)key0 * H + head) * (kDvo * 2);
+        uint64_t row0 = (uint64_t)key0;
+        if constexpr (kPaged) {
+            const int page = entry < 0 ? 0 : (entry >= pg.num_pages ? pg.num_pages - 1 : entry);
+            row0 = (uint64_t)page * pg.page_size + (uint64_t)(key0 % pg.page_size);
+        }
+        const uint8_t* kb = kseq + (row0 * H + head) * (kDqk * 2);
+        const uint8_t* vb = vseq + (row0 * H + head) * (kDvo * 2);
         uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
         if (key0 + kBN - 1 > last_key) {
             const int lim = last_key - key0;
@@ -354,12 +370,21 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
     const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
 
-    // issue cursor: the next global tile to put in flight
+    // issue cursor: the next global tile to put in flight; with paged K/V
+    // the page of that tile is read one issue ahead, so the table lookup's
+    // latency is hidden behind an iteration
     int iss_g = 0, iss_h = 0, iss_kt = 0;
+    int iss_page = 0;
+    if constexpr (kPaged) {
+        if (total_tiles > 0) iss_page = page_entry(0);
+    }
     auto issue_next = [&]() {
-        issue_tile(it.head0 + iss_h, iss_kt, iss_g % kStages);
+        issue_tile(it.head0 + iss_h, iss_kt, iss_g % kStages, iss_page);
         ++iss_g;
         if (++iss_kt == n_tiles) { iss_kt = 0; ++iss_h; }
+        if constexpr (kPaged) {
+            if (iss_g < total_tiles) iss_page = page_entry(iss_kt);
+        }
     };
     // Software pipeline: the iteration for global tile g publishes tile g+1
     // (one barrier; it also retires tile g-1), puts tile g+3 in flight into
@@ -468,14 +493,24 @@ int prefill_bf16_block_m() { return kBM; }
 
 hipError_t launch_prefill_bf16(const WorkItem* items, int64_t n_items, const void* q,
                                const void* k, const void* v, void* out, float* lse,
-                               int num_heads, float sm_scale, hipStream_t stream) {
+                               int num_heads, float sm_scale, hipStream_t stream,
+                               const PagedKv* paged) {
     if (n_items <= 0) return hipSuccess;
     if (n_items > 0x7fffffff) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, stream,
-                       items, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse,
-                       num_heads, scale_log2);
+    const PagedKv pg = paged != nullptr ? *paged : PagedKv{nullptr, 0, 0, 0};
+    if (paged != nullptr)
+        hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)n_items), dim3(kThreads), 0,
+                           stream, items, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                           static_cast<uint16_t*>(out), lse, num_heads, scale_log2, pg,
+                           pg.block_table);
+    else
+        hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)n_items), dim3(kThreads), 0,
+                           stream, items, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                           static_cast<uint16_t*>(out), lse, num_heads, scale_log2, pg,
+                           nullptr);
     return hipGetLastError();
 }
 

@@ -23,10 +23,11 @@ constexpr int kThreads = 64;
 constexpr int kBN = 32;
 constexpr float kLn2 = 0.6931471805599453f;
 
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void prefill_fp32_kernel(
     const WorkItem* __restrict__ items, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, float* __restrict__ out, float* __restrict__ lse, int num_heads,
-    float scale_log2) {
+    float scale_log2, PagedKv pg) {
     __shared__ __attribute__((aligned(16))) float ks[kBN][kDqk];
     __shared__ __attribute__((aligned(16))) float vs[kBN][kDvo];
 
@@ -51,7 +52,16 @@ __global__ __launch_bounds__(kThreads) void prefill_fp32_kernel(
 #pragma unroll
         for (int d = 0; d < kDvo; ++d) o[d] = 0.f;
         float m_run = -INFINITY, l_run = 0.f;
-        const int64_t kv_base = (int64_t)it.kv_start * H + head;
+        // K/V row (token index in the cache, head 0) of key `key`
+        auto kv_row = [&](int key) -> int64_t {
+            if constexpr (kPaged) {
+                int pgi = pg.block_table[(int64_t)it.kv_start * pg.max_pages + key / pg.page_size];
+                pgi = pgi < 0 ? 0 : (pgi >= pg.num_pages ? pg.num_pages - 1 : pgi);
+                return ((int64_t)pgi * pg.page_size + key % pg.page_size) * H;
+            } else {
+                return ((int64_t)it.kv_start + key) * H;
+            }
+        };
 
         for (int key0 = 0; key0 < it.kv_hi; key0 += kBN) {
             __syncthreads();
@@ -59,14 +69,14 @@ __global__ __launch_bounds__(kThreads) void prefill_fp32_kernel(
                 const int row = u / (kDqk / 4), c = u % (kDqk / 4);
                 const int key = key0 + row;
                 *reinterpret_cast<f32x4_t*>(&ks[row][c * 4]) =
-                    key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(k + (kv_base + (int64_t)key * H) * kDqk + c * 4)
+                    key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(k + (kv_row(key) + head) * kDqk + c * 4)
                                     : f32x4_t{};
             }
             for (int u = lane; u < kBN * (kDvo / 4); u += kThreads) {
                 const int row = u / (kDvo / 4), c = u % (kDvo / 4);
                 const int key = key0 + row;
                 *reinterpret_cast<f32x4_t*>(&vs[row][c * 4]) =
-                    key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(v + (kv_base + (int64_t)key * H) * kDvo + c * 4)
+                    key < it.kv_len ? *reinterpret_cast<const f32x4_t*>(v + (kv_row(key) + head) * kDvo + c * 4)
                                     : f32x4_t{};
             }
             __syncthreads();
@@ -114,14 +124,22 @@ int prefill_fp32_block_m() { return kThreads; }
 
 hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const void* q,
                                const void* k, const void* v, void* out, float* lse,
-                               int num_heads, float sm_scale, hipStream_t stream) {
+                               int num_heads, float sm_scale, hipStream_t stream,
+                               const PagedKv* paged) {
     if (n_items <= 0) return hipSuccess;
     if (n_items > 0x7fffffff) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(prefill_fp32_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, stream,
-                       items, static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), static_cast<float*>(out), lse, num_heads,
-                       scale_log2);
+    const PagedKv pg = paged != nullptr ? *paged : PagedKv{nullptr, 0, 0, 0};
+    if (paged != nullptr)
+        hipLaunchKernelGGL(prefill_fp32_kernel<true>, dim3((unsigned)n_items), dim3(kThreads), 0,
+                           stream, items, static_cast<const float*>(q),
+                           static_cast<const float*>(k), static_cast<const float*>(v),
+                           static_cast<float*>(out), lse, num_heads, scale_log2, pg);
+    else
+        hipLaunchKernelGGL(prefill_fp32_kernel<false>, dim3((unsigned)n_items), dim3(kThreads), 0,
+                           stream, items, static_cast<const float*>(q),
+                           static_cast<const float*>(k), static_cast<const float*>(v),
+                           static_cast<float*>(out), lse, num_heads, scale_log2, pg);
     return hipGetLastError();
 }
 

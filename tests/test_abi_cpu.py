@@ -273,3 +273,28 @@ def test_device_plan_rejects_invalid_arguments_before_any_hip_call():
     assert call(max_tq=-1) == 1
     assert call(max_tq=(1 << 31) // 4 + 1) == 2        # tokens x heads beyond 2^31
     assert call(batch=0) == 0                          # no-op
+
+
+def test_paged_prefill_rejects_invalid_arguments_before_any_hip_call():
+    import numpy as np
+    l = mra.lib()
+    qo = np.array([0, 40, 100], dtype=np.int32)
+    kv = np.array([0, 64, 192], dtype=np.int32)      # contexts of 64 and 128 keys
+    base = dict(q=16, k=16, v=16, qo=qo.ctypes.data, kv=kv.ctypes.data, table=16, max_pages=2,
+                page=64, pages=8, batch=2, heads=4, causal=1, scale=0.1, dtype=0, out=16, lse=16,
+                stream=None)
+    order = ["q", "k", "v", "qo", "kv", "table", "max_pages", "page", "pages", "batch", "heads",
+             "causal", "scale", "dtype", "out", "lse", "stream"]
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return l.mla_ragged_prefill_paged(*[a[n] for n in order])
+
+    assert call(page=48) == 1                     # not a multiple of 32
+    assert call(page=0) == 1
+    assert call(max_pages=1) == 1                 # 128 keys do not fit 1 page of 64
+    assert call(table=None) == 1
+    assert call(table=18) == 1                    # misaligned table
+    assert call(pages=0) == 1
+    assert call(scale=-1.0) == 1
+    assert call(dtype=3) == 2
