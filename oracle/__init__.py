@@ -44,6 +44,8 @@ def bind(lib):
     P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.oracle_prefill.argtypes = [P, P, P, I, P, P, I, I, I, I, I, D, P, I64, P, P]
     lib.oracle_prefill.restype = I
+    lib.oracle_absorbed.argtypes = [P, P, I, P, P, I, I, I, I, I, D, P, I64, P, P]
+    lib.oracle_absorbed.restype = I
     lib.oracle_merge.argtypes = [P, P, P, P, I, I, I64, I, P, P]
     lib.oracle_merge.restype = I
     lib.oracle_decompress.argtypes = [P, P, P, P, I, I64, I, I, I, I, I, P, I64, P, P]
@@ -98,6 +100,40 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qo_indptr, kv_ind
                             out.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise RuntimeError("oracle_prefill failed")
+    return torch.from_numpy(out), torch.from_numpy(lse)
+
+
+def absorbed(q: torch.Tensor, kv: torch.Tensor, qo_indptr, kv_indptr, causal: bool,
+             sm_scale: float, dvo: int = 512, rows: Optional[Sequence[int]] = None):
+    """Weight-absorbed MLA over the latent cache: q [Tq, H, 576], kv [Tk, 576]
+    (one shared row per token, value = its first dvo dims). O [n, H, dvo] and
+    LSE [n, H] in fp64."""
+    lib = _load()
+    q, kv = _host(q), _host(kv)
+    if q.dtype != kv.dtype or q.dtype not in _DT:
+        raise TypeError("q and kv must share one of bf16 / fp32 / fp64")
+    heads, dqk = q.shape[1], q.shape[2]
+    if kv.dim() != 2 or kv.shape[1] != dqk:
+        raise ValueError("kv must be [Tk, dqk]")
+    qo = _i32(qo_indptr)
+    kvi = _i32(kv_indptr)
+    batch = len(qo) - 1
+    if rows is None:
+        n = int(qo[-1])
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = len(rows_arr)
+    out = np.zeros((n, heads, dvo), dtype=np.float64)
+    lse = np.zeros((n, heads), dtype=np.float64)
+    if n == 0 or batch == 0:
+        return torch.from_numpy(out), torch.from_numpy(lse)
+    rc = lib.oracle_absorbed(q.data_ptr(), kv.data_ptr(), _DT[q.dtype], qo.ctypes.data,
+                             kvi.ctypes.data, batch, heads, dqk, dvo, int(bool(causal)),
+                             float(sm_scale), None if rows_arr is None else rows_arr.ctypes.data,
+                             n, out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_absorbed failed")
     return torch.from_numpy(out), torch.from_numpy(lse)
 
 

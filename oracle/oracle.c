@@ -154,6 +154,80 @@ int oracle_prefill(const void *q, const void *k, const void *v, int dtype,
 }
 
 /*
+ * Weight-absorbed MLA attention over the latent cache (multi-query: one
+ * shared key/value row per token). The query of head h is the 576-dim
+ * absorbed query [q_nope W_UK_h | q_rope]; the key of token j is its cache
+ * row kv[j] = [c_kv | k_rope] (576 dims), the value is the first dvo (512)
+ * dims of the same row (the latent), and the output stays in the latent
+ * space ("[DeepseekR1] How ragged prefill manage kv_cache?", sglang issue
+ * 3849: the absorbed path, forward_absorb, that attends the latent cache
+ * directly). Same visible-key rule, scaling and LSE as oracle_prefill.
+ *   q [Tq, H, dqk] and kv [Tk, dqk] of dtype `dtype`; dvo <= dqk.
+ *   rows: query token indices (n_rows of them), or NULL for all Tq.
+ *   out [n_rows, H, dvo] and lse [n_rows, H] in fp64.
+ */
+int oracle_absorbed(const void *q, const void *kv, int dtype, const int32_t *qo_indptr,
+                    const int32_t *kv_indptr, int batch, int num_heads, int dqk, int dvo,
+                    int causal, double sm_scale, const int64_t *rows, int64_t n_rows,
+                    double *out, double *lse) {
+    if (batch < 1 || num_heads < 1 || dqk < 1 || dvo < 1 || dvo > dqk) return -1;
+    if (rows == NULL) n_rows = qo_indptr[batch];
+    int64_t max_kv = 0;
+    for (int b = 0; b < batch; ++b) {
+        int64_t n = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+        if (n > max_kv) max_kv = n;
+    }
+    int failed = 0;
+#pragma omp parallel reduction(|:failed)
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)(max_kv > 0 ? max_kv : 1));
+        if (sc == NULL) failed = 1;
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            for (int h = 0; h < num_heads; ++h) {
+                if (sc == NULL) continue;
+                int64_t t = rows ? rows[r] : r;
+                int b = owner(qo_indptr, batch, t);
+                int64_t qs = qo_indptr[b], ks = kv_indptr[b];
+                int64_t qo_len = (int64_t)qo_indptr[b + 1] - qs;
+                int64_t kv_len = (int64_t)kv_indptr[b + 1] - ks;
+                int64_t nv = visible_keys(t - qs, qo_len, kv_len, causal);
+                double *o_row = out + ((size_t)r * num_heads + h) * dvo;
+                double *lse_out = lse + (size_t)r * num_heads + h;
+                if (nv == 0) {
+                    for (int d = 0; d < dvo; ++d) o_row[d] = 0.0;
+                    *lse_out = -INFINITY;
+                    continue;
+                }
+                /* pass 1: scaled scores against the shared cache rows */
+                int64_t q_at = ((int64_t)t * num_heads + h) * dqk;
+                for (int64_t j = 0; j < nv; ++j) {
+                    int64_t row_at = (ks + j) * dqk;
+                    double acc = 0.0;
+                    for (int d = 0; d < dqk; ++d)
+                        acc += load_elem(q, dtype, q_at + d) * load_elem(kv, dtype, row_at + d);
+                    sc[j] = sm_scale * acc;
+                }
+                /* pass 2: softmax weights, LSE, weighted sum of the latent parts */
+                double top = sc[0];
+                for (int64_t j = 1; j < nv; ++j) if (sc[j] > top) top = sc[j];
+                double den = 0.0;
+                for (int64_t j = 0; j < nv; ++j) { sc[j] = exp(sc[j] - top); den += sc[j]; }
+                *lse_out = top + log(den);
+                for (int d = 0; d < dvo; ++d) o_row[d] = 0.0;
+                for (int64_t j = 0; j < nv; ++j) {
+                    double w = sc[j] / den;
+                    int64_t latent_at = (ks + j) * dqk;
+                    for (int d = 0; d < dvo; ++d) o_row[d] += w * load_elem(kv, dtype, latent_at + d);
+                }
+            }
+        }
+        free(sc);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
  * Merge two attention states over disjoint key sets.
  *   o_a, o_b [rows, dim] of dtype o_dtype; lse_a, lse_b [rows] of dtype lse_dtype.
  *   o [rows, dim], lse [rows] in fp64.

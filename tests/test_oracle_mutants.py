@@ -34,6 +34,11 @@ MUTANTS = {
     "decompress_w_transposed": (
         "load_elem(w_uk, dtype, (int64_t)c * num_heads * dnope + (int64_t)h * dnope + d)",
         "load_elem(w_uk, dtype, (int64_t)d * num_heads * dnope + (int64_t)h * dnope + c)"),
+    "absorbed_value_from_the_wrong_dims": ("int64_t latent_at = (ks + j) * dqk;",
+                                           "int64_t latent_at = (ks + j) * dqk + (dqk - dvo);"),
+    "absorbed_row_stride": ("int64_t row_at = (ks + j) * dqk;", "int64_t row_at = (ks + j) * dvo;"),
+    "absorbed_head_stride_dropped": ("int64_t q_at = ((int64_t)t * num_heads + h) * dqk;",
+                                     "int64_t q_at = ((int64_t)t * num_heads) * dqk;"),
     "decompress_rope_not_copied": ("k_row[dnope + d] = load_elem(k_rope, dtype, t * drope + d);",
                                    "k_row[dnope + d] = 0.0;"),
 }
@@ -50,6 +55,9 @@ PIN_TESTS = [
     pins.test_chunked_prefill_equals_one_bottom_right_causal_call,
     pins.test_decompress_one_hot_latent_picks_weight_rows,
     pins.test_decompress_matches_float64_matmul,
+    pins.test_absorbed_single_visible_key_returns_that_latent_row,
+    pins.test_absorbed_equal_scores_average_the_latent_rows,
+    lambda: pins.test_absorbed_brute_force_library_softmax(True),
 ]
 
 

@@ -329,3 +329,89 @@ def test_decompress_matches_float64_matmul():
     assert torch.allclose(v, mv, atol=1e-12, rtol=0)
     ks, vs = oracle.decompress(c_kv, k_rope, w_uk, w_uv, 2, rows=[6, 2])
     assert torch.equal(ks, k[[6, 2]]) and torch.equal(vs, v[[6, 2]])
+
+
+# ---------------------------------------------------------------------------
+# weight-absorbed MLA over the latent cache (one shared 576-dim row per token)
+# ---------------------------------------------------------------------------
+
+def _absorbed_case(lens_q, lens_kv, heads, seed, dtype=torch.float32):
+    g = torch.Generator().manual_seed(seed)
+    tq, tk = sum(lens_q), sum(lens_kv)
+    q = workloads.randn((tq, heads, 576), g, dtype, "cpu")
+    kv = workloads.randn((tk, 576), g, dtype, "cpu")
+    return q, kv, workloads.indptr_from_lengths(lens_q), workloads.indptr_from_lengths(lens_kv)
+
+
+def test_absorbed_single_visible_key_returns_that_latent_row():
+    q, kv, qo, kvi = _absorbed_case([3, 17, 1], [3, 17, 1], 4, seed=50)
+    scale = 192 ** -0.5
+    o, lse = oracle.absorbed(q, kv, qo, kvi, True, scale)
+    for b in range(3):
+        t, j = qo[b], kvi[b]
+        for h in range(4):
+            assert torch.equal(o[t, h], kv[j, :512].double())
+            s = scale * float(q[t, h].double() @ kv[j].double())
+            assert abs(float(lse[t, h]) - s) < 1e-12
+
+
+def test_absorbed_equal_scores_average_the_latent_rows():
+    # zero latent part of every query and one shared RoPE part for every key:
+    # all visible scores are equal, so O is the mean of the visible latent rows
+    lens_q, lens_kv = [5, 9], [7, 9]
+    q, kv, qo, kvi = _absorbed_case(lens_q, lens_kv, 3, seed=51)
+    q[:, :, :512] = 0
+    kv[:, 512:] = kv[0, 512:]
+    scale = 0.3
+    o, lse = oracle.absorbed(q, kv, qo, kvi, True, scale)
+    for b in range(2):
+        for i in range(lens_q[b]):
+            n = min(lens_kv[b], max(0, lens_kv[b] - lens_q[b] + i + 1))
+            t = qo[b] + i
+            for h in range(3):
+                mean = kv[kvi[b]:kvi[b] + n, :512].double().mean(0)
+                assert torch.allclose(o[t, h], mean, atol=1e-12, rtol=0)
+                s = scale * float(q[t, h, 512:].double() @ kv[0, 512:].double())
+                assert abs(float(lse[t, h]) - (s + math.log(n))) < 1e-12
+
+
+def _absorbed_brute(q, kv, qo, kvi, causal, scale, dvo=512):
+    tq, heads = q.shape[0], q.shape[1]
+    o = torch.zeros(tq, heads, dvo, dtype=torch.float64)
+    lse = torch.full((tq, heads), -math.inf, dtype=torch.float64)
+    for b in range(len(qo) - 1):
+        ql, kl = qo[b + 1] - qo[b], kvi[b + 1] - kvi[b]
+        if ql == 0 or kl == 0:
+            continue
+        keys = kv[kvi[b]:kvi[b + 1]].double()
+        for h in range(heads):
+            s = (q[qo[b]:qo[b + 1], h].double() @ keys.T) * scale
+            if causal:
+                keep = torch.tril(torch.ones(ql, kl, dtype=torch.bool), diagonal=kl - ql)
+                s = s.masked_fill(~keep, -math.inf)
+            rows = torch.isfinite(s).any(1)
+            o[qo[b]:qo[b + 1], h][rows] = torch.softmax(s[rows], dim=1) @ keys[:, :dvo]
+            lse[qo[b]:qo[b + 1], h][rows] = torch.logsumexp(s[rows], dim=1)
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_absorbed_brute_force_library_softmax(causal):
+    q, kv, qo, kvi = _absorbed_case([5, 0, 12, 3], [9, 4, 12, 1], 3, seed=52)
+    scale = 192 ** -0.5
+    o, lse = oracle.absorbed(q, kv, qo, kvi, causal, scale)
+    bo, bl = _absorbed_brute(q, kv, qo, kvi, causal, scale)
+    assert torch.allclose(o, bo, atol=1e-12, rtol=0)
+    assert torch.equal(torch.isinf(lse), torch.isinf(bl))
+    fin = torch.isfinite(bl)
+    assert torch.allclose(lse[fin], bl[fin], atol=1e-12, rtol=0)
+
+
+def test_absorbed_equals_mha_over_a_broadcast_cache():
+    q, kv, qo, kvi = _absorbed_case([6, 13], [20, 13], 2, seed=53)
+    scale = 0.05
+    o, lse = oracle.absorbed(q, kv, qo, kvi, True, scale)
+    k = kv[:, None, :].expand(-1, 2, -1).contiguous()
+    v = kv[:, None, :512].expand(-1, 2, -1).contiguous()
+    mo, ml = oracle.prefill(q, k, v, qo, kvi, True, scale)
+    assert torch.allclose(o, mo, atol=1e-12, rtol=0) and torch.allclose(lse, ml, atol=1e-12, rtol=0)
