@@ -273,6 +273,45 @@ int mla_decompress_kv(const void *c_kv, const void *k_rope, const void *w_uk, co
                       int64_t num_tokens, int32_t num_heads, void *k_out, void *v_out,
                       void *stream);
 
+/*
+ * Weight-absorbed MLA prefill over the latent cache (sglang issue 3849,
+ * "[DeepseekR1] How ragged prefill manage kv_cache?": the absorb path that
+ * attends the compressed cache directly instead of decompressing it). Each
+ * query token t and head h carries an absorbed query of 576 dims (latent
+ * 512 | RoPE 64); each key token j one cache row kv[j] = [c_kv | k_rope],
+ * shared by all heads, whose first 512 dims are also its value:
+ *   s[t,h,j]  = sm_scale * q[t,h,:] . kv[j,:]
+ *   O[t,h,:]  = sum_j softmax_j(s[t,h,j]) kv[j,0:512]
+ *   lse[t,h]  = ln sum_j e^s[t,h,j]
+ * over the keys j visible to token t of its sequence (bottom-right causal:
+ * j < kv_len - qo_len + i + 1 for the sequence's i-th query; all keys when
+ * non-causal). A token with no visible key gets O = 0 and lse = -inf. bf16
+ * inputs and outputs, fp32 accumulation and softmax.
+ *
+ *   q     device bf16 [Tq, H, 576], Tq = qo_indptr[batch].
+ *   kv    device bf16 [Tk, 576],    Tk = kv_indptr[batch].
+ *   qo_indptr, kv_indptr  HOST int32 [batch + 1], indptr[0] = 0,
+ *         non-decreasing; Tq * H < 2^31.
+ *   out   device bf16 [Tq, H, 512];  lse device fp32 [Tq, H] or NULL.
+ *   All device pointers 16-byte aligned. The call plans on the host (the
+ *   work list is kept per (device, stream) and reused) and enqueues one
+ *   kernel on `stream`; it returns before the kernel ends. Calls on one
+ *   stream must come from one thread at a time.
+ */
+int mla_absorbed_prefill(const void *q, const void *kv, const int32_t *qo_indptr,
+                         const int32_t *kv_indptr, int32_t batch, int32_t num_heads,
+                         int32_t causal, float sm_scale, void *out, float *lse, void *stream);
+
+/*
+ * Host-only view of the absorbed prefill's work list (no HIP call): writes
+ * *n_items and, if dst is non-NULL and capacity_items suffices, the items
+ * as 8 int32 each: {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len,
+ * diag_base, 0}, flat row = token * H + head; n_rows = 0 marks padding.
+ */
+int mla_absorbed_plan_items(const int32_t *qo_indptr, const int32_t *kv_indptr, int32_t batch,
+                            int32_t num_heads, int32_t causal, int32_t *dst,
+                            int64_t capacity_items, int64_t *n_items);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,7 @@ Functions mirror the C entry points:
   ragged_prefill(q, k, v, qo_indptr, kv_indptr, causal, sm_scale, return_lse=True)
   merge_state(o_a, lse_a, o_b, lse_b, out=None, out_lse=None)
   decompress_kv(c_kv, k_rope, w_uk, w_uv, num_heads)
+  absorbed_prefill(q, kv, qo_indptr, kv_indptr, causal, sm_scale, return_lse=True)
   Plan: plan() once per batch, run() once per layer.
 """
 from __future__ import annotations
@@ -21,8 +22,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-__all__ = ["ragged_prefill", "ragged_prefill_paged", "merge_state", "decompress_kv", "Plan", "DevicePlan", "MlaError", "lib",
-           "LIB_PATH", "DQK", "DVO", "EXPORTED_SYMBOLS"]
+__all__ = ["ragged_prefill", "ragged_prefill_paged", "merge_state", "decompress_kv",
+           "absorbed_prefill", "absorbed_plan_items", "Plan", "DevicePlan", "MlaError", "lib",
+           "LIB_PATH", "DQK", "DVO", "DLAT", "DROPE", "EXPORTED_SYMBOLS"]
 
 DQK, DVO, DLAT, DROPE = 192, 128, 512, 64
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +38,7 @@ EXPORTED_SYMBOLS = [
     "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_set_xcds",
     "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
     "mla_ragged_prefill_device_plan", "mla_ragged_prefill_paged",
-    "mla_merge_state", "mla_decompress_kv",
+    "mla_merge_state", "mla_decompress_kv", "mla_absorbed_prefill", "mla_absorbed_plan_items",
 ]
 
 
@@ -85,6 +87,9 @@ def lib():
                                       P, P], ctypes.c_int),
         "mla_merge_state": ([P, P, P, P, P, P, I64, I32, I32, P], ctypes.c_int),
         "mla_decompress_kv": ([P, P, P, P, I64, I32, P, P, P], ctypes.c_int),
+        "mla_absorbed_prefill": ([P, P, P, P, I32, I32, I32, F, P, P, P], ctypes.c_int),
+        "mla_absorbed_plan_items": ([P, P, I32, I32, I32, P, I64, ctypes.POINTER(I64)],
+                                    ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(l, name)
@@ -387,3 +392,62 @@ def decompress_kv(c_kv: torch.Tensor, k_rope: torch.Tensor, w_uk: torch.Tensor,
                                        _stream(c_kv.device)),
                "mla_decompress_kv")
     return k_out, v_out
+
+
+def absorbed_plan_items(qo_indptr, kv_indptr, num_heads: int, causal: bool) -> np.ndarray:
+    """Host work list of the absorbed prefill: int32 [n_items, 8] rows
+    {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len, diag_base, 0}."""
+    qo, kv = _indptr(qo_indptr), _indptr(kv_indptr)
+    if len(qo) != len(kv) or len(qo) < 1:
+        raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+    l = lib()
+    n = ctypes.c_int64(0)
+    _check(l.mla_absorbed_plan_items(qo.ctypes.data, kv.ctypes.data, len(qo) - 1, int(num_heads),
+                                     int(bool(causal)), None, 0, ctypes.byref(n)),
+           "mla_absorbed_plan_items")
+    buf = np.zeros((max(n.value, 1), 8), dtype=np.int32)
+    _check(l.mla_absorbed_plan_items(qo.ctypes.data, kv.ctypes.data, len(qo) - 1, int(num_heads),
+                                     int(bool(causal)), buf.ctypes.data, buf.shape[0],
+                                     ctypes.byref(n)),
+           "mla_absorbed_plan_items")
+    return buf[: n.value]
+
+
+def absorbed_prefill(q: torch.Tensor, kv: torch.Tensor, qo_indptr, kv_indptr, causal: bool,
+                     sm_scale: float, return_lse: bool = True,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Weight-absorbed MLA prefill over the latent cache (bf16): q [Tq,H,576]
+    absorbed queries, kv [Tk,576] latent cache rows (c_kv | k_rope) on the
+    GPU; host indptrs of length batch+1. Returns out [Tq,H,512] (and lse
+    [Tq,H] fp32, natural log) on the current stream."""
+    _dev_tensor(q, "q")
+    _dev_tensor(kv, "kv")
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise ValueError("q and kv must be bf16")
+    dk = DLAT + DROPE
+    if q.dim() != 3 or q.shape[2] != dk or kv.dim() != 2 or kv.shape[1] != dk:
+        raise ValueError("q must be [Tq,H,576] and kv [Tk,576]")
+    qo, kvp = _indptr(qo_indptr), _indptr(kv_indptr)
+    if len(qo) != len(kvp) or len(qo) < 1:
+        raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+    if qo[-1] != q.shape[0] or kvp[-1] != kv.shape[0]:
+        raise ValueError("indptr totals do not match the token counts of q / kv")
+    tq, heads = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((tq, heads, DLAT), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((tq, heads), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, "out")
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (tq, heads, DLAT):
+        raise ValueError("out must be bf16 [Tq,H,512]")
+    if return_lse:
+        _dev_tensor(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (tq, heads):
+            raise ValueError("lse must be fp32 [Tq,H]")
+    with torch.cuda.device(q.device):
+        _check(lib().mla_absorbed_prefill(_ptr(q), _ptr(kv), qo.ctypes.data, kvp.ctypes.data,
+                                          len(qo) - 1, heads, int(bool(causal)), float(sm_scale),
+                                          _ptr(out), _ptr(lse) if return_lse else None,
+                                          _stream(q.device)),
+               "mla_absorbed_prefill")
+    return (out, lse) if return_lse else out

@@ -24,7 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # the LDS DMA asm in the prefill kernel declares M0 clobbered on purpose
           "-Wno-inline-asm"]
 SOURCES = ["abi.cpp", "planner.cpp", "prefill_bf16.hip", "prefill_fp32.hip", "merge.hip",
-           "decompress.hip", "device_plan.hip"]
+           "decompress.hip", "device_plan.hip", "prefill_absorbed.hip"]
 
 
 def _compile(src: str, extra=()) -> str:

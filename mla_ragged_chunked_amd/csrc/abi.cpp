@@ -38,12 +38,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Pinned host staging + device buffer for one work list. Grow-only.
 // A ring of pinned slots lets several uploads be in flight on a stream
 // before the host has to wait for the oldest copy to finish.
+template <class Item>
 struct DeviceWorkList {
     static constexpr int kRing = 4;
-    WorkItem* dev = nullptr;
+    Item* dev = nullptr;
     size_t dev_cap = 0;             // items
     int device = -1;
-    WorkItem* pinned[kRing] = {};
+    Item* pinned[kRing] = {};
     size_t pinned_cap[kRing] = {};
     hipEvent_t done[kRing] = {};
     bool pending[kRing] = {};
@@ -67,7 +68,7 @@ struct DeviceWorkList {
     }
 
     // Asynchronously copy `items` to `dev` on `stream`.
-    int upload(const std::vector<WorkItem>& items, hipStream_t stream) {
+    int upload(const std::vector<Item>& items, hipStream_t stream) {
         int cur = -1;
         hipError_t e = hipGetDevice(&cur);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -89,7 +90,7 @@ struct DeviceWorkList {
                 dev = nullptr;
                 dev_cap = 0;
             }
-            e = hipMalloc(&dev, n * sizeof(WorkItem));
+            e = hipMalloc(&dev, n * sizeof(Item));
             if (e != hipSuccess) { dev = nullptr; return fail(MLA_ENOMEM, "hipMalloc of the work list failed"); }
             dev_cap = n;
         }
@@ -105,7 +106,7 @@ struct DeviceWorkList {
             if (pinned[slot]) (void)hipHostFree(pinned[slot]);
             pinned[slot] = nullptr;
             pinned_cap[slot] = 0;
-            e = hipHostMalloc(reinterpret_cast<void**>(&pinned[slot]), items.size() * sizeof(WorkItem),
+            e = hipHostMalloc(reinterpret_cast<void**>(&pinned[slot]), items.size() * sizeof(Item),
                               hipHostMallocDefault);
             if (e != hipSuccess) { pinned[slot] = nullptr; return fail(MLA_ENOMEM, "hipHostMalloc of staging failed"); }
             pinned_cap[slot] = items.size();
@@ -114,8 +115,8 @@ struct DeviceWorkList {
             e = hipEventCreateWithFlags(&done[slot], hipEventDisableTiming);
             if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
         }
-        std::memcpy(pinned[slot], items.data(), items.size() * sizeof(WorkItem));
-        e = hipMemcpyAsync(dev, pinned[slot], items.size() * sizeof(WorkItem),
+        std::memcpy(pinned[slot], items.data(), items.size() * sizeof(Item));
+        e = hipMemcpyAsync(dev, pinned[slot], items.size() * sizeof(Item),
                            hipMemcpyHostToDevice, stream);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of the work list");
         e = hipEventRecord(done[slot], stream);
@@ -136,7 +137,7 @@ struct mla_plan {
     bool paged = false;           // items carry the sequence index in kv_start
     bool planned = false;
     bool uploaded = false;
-    DeviceWorkList dwl;
+    DeviceWorkList<WorkItem> dwl;
 };
 
 namespace {
@@ -288,6 +289,33 @@ int oneshot(const void* q, const void* k, const void* v, const int32_t* qo_indpt
     p->uploaded = false;
     if (int s = mla_plan_upload(p, stream)) return s;
     return do_run(p, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream), paged);
+}
+
+// Weight-absorbed prefill: host-planned work list kept per (device, stream).
+struct AbsorbedState {
+    std::vector<mla::LatentItem> items;
+    DeviceWorkList<mla::LatentItem> dwl;
+};
+std::mutex g_absorbed_mu;
+std::map<std::pair<int, void*>, AbsorbedState*>* g_absorbed = nullptr;
+
+int absorbed_plan(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_heads,
+                  int32_t causal, std::vector<mla::LatentItem>& items) {
+    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
+    if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
+    if (num_heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
+    if (batch > 0 && (qo == nullptr || kv == nullptr)) return fail(MLA_EINVAL, "indptr is NULL");
+    if (batch > 0 && static_cast<int64_t>(kv[batch]) * (MLA_LATENT_DIM + MLA_ROPE_DIM) > INT64_C(1) << 40)
+        return fail(MLA_EUNSUPPORTED, "latent cache too large");
+    std::string err;
+    try {
+        if (!mla::build_latent_work_list(qo, kv, batch, num_heads, causal != 0,
+                                         mla::prefill_absorbed_block_m(), 8, items, err))
+            return fail(MLA_EINVAL, err);
+    } catch (const std::bad_alloc&) {
+        return fail(MLA_ENOMEM, "host allocation of the work list failed");
+    }
+    return MLA_OK;
 }
 
 }  // namespace
@@ -502,6 +530,63 @@ int mla_decompress_kv(const void* c_kv, const void* k_rope, const void* w_uk, co
     hipError_t e = mla::launch_decompress(c_kv, k_rope, w_uk, w_uv, num_tokens, num_heads, k_out,
                                           v_out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decompression kernel launch");
+    return MLA_OK;
+}
+
+int mla_absorbed_plan_items(const int32_t* qo_indptr, const int32_t* kv_indptr, int32_t batch,
+                            int32_t num_heads, int32_t causal, int32_t* dst,
+                            int64_t capacity_items, int64_t* n_items) {
+    if (n_items == nullptr) return fail(MLA_EINVAL, "n_items is NULL");
+    std::vector<mla::LatentItem> items;
+    if (int s = absorbed_plan(qo_indptr, kv_indptr, batch, num_heads, causal, items)) return s;
+    *n_items = static_cast<int64_t>(items.size());
+    if (dst == nullptr) return MLA_OK;
+    if (capacity_items < static_cast<int64_t>(items.size()))
+        return fail(MLA_EINVAL, "capacity too small for the work list");
+    if (!items.empty()) std::memcpy(dst, items.data(), items.size() * sizeof(mla::LatentItem));
+    return MLA_OK;
+}
+
+int mla_absorbed_prefill(const void* q, const void* kv, const int32_t* qo_indptr,
+                         const int32_t* kv_indptr, int32_t batch, int32_t num_heads,
+                         int32_t causal, float sm_scale, void* out, float* lse, void* stream) {
+    if (int s = check_scale(sm_scale)) return s;
+    std::vector<mla::LatentItem> items;
+    if (int s = absorbed_plan(qo_indptr, kv_indptr, batch, num_heads, causal, items)) return s;
+    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
+    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
+    if (tq > 0 && (q == nullptr || out == nullptr))
+        return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
+    if (tk > 0 && kv == nullptr) return fail(MLA_EINVAL, "kv must be non-NULL when there are keys");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
+        return fail(MLA_EINVAL, "q, kv, out and lse must be 16-byte aligned");
+    if (items.empty()) return MLA_OK;
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    AbsorbedState* st = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_absorbed_mu);
+        if (g_absorbed == nullptr)
+            g_absorbed = new (std::nothrow) std::map<std::pair<int, void*>, AbsorbedState*>();
+        if (g_absorbed == nullptr) return fail(MLA_ENOMEM, "absorbed plan table");
+        auto key = std::make_pair(dev, stream);
+        auto it = g_absorbed->find(key);
+        if (it == g_absorbed->end()) {
+            st = new (std::nothrow) AbsorbedState();
+            if (st == nullptr) return fail(MLA_ENOMEM, "absorbed plan");
+            (*g_absorbed)[key] = st;
+        } else {
+            st = it->second;
+        }
+    }
+    st->items.swap(items);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int r = st->dwl.upload(st->items, s)) return r;
+    e = mla::launch_prefill_absorbed(st->dwl.dev, static_cast<int64_t>(st->items.size()), q, kv,
+                                     out, lse, num_heads, sm_scale, s);
+    if (e != hipSuccess) return hip_fail(e, "absorbed prefill kernel launch");
     return MLA_OK;
 }
 

@@ -44,6 +44,23 @@ struct PagedKv {
     int32_t num_pages;
 };
 
+// One work item of the weight-absorbed (latent-cache) prefill: a tile of
+// consecutive flat query rows of one sequence, flat row rho = token * H +
+// head. Row rho sees keys [0, lim(rho)) of its sequence,
+//   lim(rho) = min(kv_len, max(0, diag_base + (rho - seq_row0) / H + 1)),
+// diag_base = kv_len - qo_len when causal, kv_len otherwise. 32 bytes.
+struct LatentItem {
+    int32_t row0;       // first flat row of the tile
+    int32_t n_rows;     // rows in the tile; 0 = padding item (kernel returns)
+    int32_t seq_row0;   // flat row of the sequence's first token, head 0
+    int32_t kv_hi;      // lim of the tile's last row: keys the tile visits
+    int32_t kv_start;   // global token index of the sequence's first key
+    int32_t kv_len;
+    int32_t diag_base;
+    int32_t reserved;
+};
+static_assert(sizeof(LatentItem) == 32, "latent work item layout");
+
 // Query-tile heights of the two prefill kernels (each kernel file owns its
 // tile shape; the planner asks for it).
 int prefill_bf16_block_m();
@@ -58,6 +75,13 @@ int prefill_fp32_block_m();
 bool build_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
                      int num_heads, bool causal, int block_m, int n_xcd, int heads_per_item,
                      std::vector<WorkItem>& out, std::string& err, bool kv_start_is_seq = false);
+
+// Work list of the weight-absorbed prefill (host only): tiles of `block_m`
+// flat rows, grouped and ordered for the XCDs like build_work_list.
+bool build_latent_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                            int num_heads, bool causal, int block_m, int n_xcd,
+                            std::vector<LatentItem>& out, std::string& err);
+int prefill_absorbed_block_m();
 
 // Device-side partitioner (device_plan.hip). The workspace holds, at these
 // byte offsets: a flag word (nonzero = some sequence had invalid indptrs and
@@ -83,6 +107,9 @@ hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const voi
                                const void* k, const void* v, void* out, float* lse,
                                int num_heads, float sm_scale, hipStream_t stream,
                                const PagedKv* paged = nullptr);
+hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, const void* q,
+                                   const void* kv, void* out, float* lse, int num_heads,
+                                   float sm_scale, hipStream_t stream);
 hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b,
                         const float* lse_b, void* o, float* lse, int64_t num_rows,
                         int dtype_bf16, hipStream_t stream);

@@ -142,4 +142,91 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
     return true;
 }
 
+// Weight-absorbed prefill: every head of a token reads the same latent
+// cache rows, so a sequence's work is its flat (token, head) rows cut into
+// tiles of block_m rows. Groups are runs of at most kLatentGroupTiles
+// consecutive tiles of one sequence (heaviest tiles first), so a long
+// sequence spreads over several XCDs while each group still shares one L2;
+// groups are dealt and laid out exactly as above.
+bool build_latent_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_heads,
+                            bool causal, int block_m, int n_xcd, std::vector<LatentItem>& out,
+                            std::string& err) {
+    constexpr size_t kLatentGroupTiles = 256;
+    out.clear();
+    if (batch < 0) { err = "batch must be >= 0"; return false; }
+    if (num_heads < 1 || num_heads > 65535) { err = "num_heads must be in [1, 65535]"; return false; }
+    if (block_m < 1) { err = "block_m must be >= 1"; return false; }
+    if (n_xcd < 1 || n_xcd > 64) { err = "n_xcd must be in [1, 64]"; return false; }
+    if (batch == 0) return true;
+    if (qo == nullptr || kv == nullptr) { err = "indptr pointer is NULL"; return false; }
+    if (qo[0] != 0 || kv[0] != 0) { err = "indptr[0] must be 0"; return false; }
+    for (int b = 0; b < batch; ++b) {
+        if (qo[b + 1] < qo[b]) { err = "qo_indptr must be non-decreasing"; return false; }
+        if (kv[b + 1] < kv[b]) { err = "kv_indptr must be non-decreasing"; return false; }
+    }
+    if (static_cast<int64_t>(qo[batch]) * num_heads > 0x7fffffffLL) {
+        err = "total query rows (tokens x heads) must be < 2^31";
+        return false;
+    }
+
+    struct LTile { LatentItem item; int64_t cost; };
+    std::vector<LTile> tiles;
+    struct Group { size_t begin, end; int64_t cost; };
+    std::vector<Group> groups;
+    for (int b = 0; b < batch; ++b) {
+        const int32_t qo_len = qo[b + 1] - qo[b];
+        const int32_t kv_len = kv[b + 1] - kv[b];
+        const int32_t seq_row0 = qo[b] * num_heads;
+        const int32_t n_rows_seq = qo_len * num_heads;
+        const int32_t diag_base = causal ? kv_len - qo_len : kv_len;
+        const size_t begin = tiles.size();
+        for (int32_t r0 = 0; r0 < n_rows_seq; r0 += block_m) {
+            LTile t;
+            t.item.row0 = seq_row0 + r0;
+            t.item.n_rows = std::min(block_m, n_rows_seq - r0);
+            t.item.seq_row0 = seq_row0;
+            const int64_t last_tok = (r0 + t.item.n_rows - 1) / num_heads;
+            const int64_t lim_last = static_cast<int64_t>(diag_base) + last_tok + 1;
+            t.item.kv_hi = static_cast<int32_t>(std::min<int64_t>(kv_len, std::max<int64_t>(0, lim_last)));
+            t.item.kv_start = kv[b];
+            t.item.kv_len = kv_len;
+            t.item.diag_base = diag_base;
+            t.item.reserved = 0;
+            t.cost = t.item.kv_hi + kTileFixedCost;
+            tiles.push_back(t);
+        }
+        std::stable_sort(tiles.begin() + begin, tiles.end(),
+                         [](const LTile& a, const LTile& c) { return a.cost > c.cost; });
+        for (size_t g0 = begin; g0 < tiles.size(); g0 += kLatentGroupTiles) {
+            const size_t g1 = std::min(tiles.size(), g0 + kLatentGroupTiles);
+            int64_t c = 0;
+            for (size_t i = g0; i < g1; ++i) c += tiles[i].cost;
+            groups.push_back({g0, g1, c});
+        }
+    }
+    if (tiles.empty()) return true;
+    std::stable_sort(groups.begin(), groups.end(),
+                     [](const Group& a, const Group& c) { return a.cost > c.cost; });
+
+    std::vector<std::vector<const Group*>> bins(n_xcd);
+    std::vector<int64_t> load(n_xcd, 0);
+    std::vector<size_t> count(n_xcd, 0);
+    for (const Group& g : groups) {
+        int best = 0;
+        for (int x = 1; x < n_xcd; ++x)
+            if (load[x] < load[best]) best = x;
+        bins[best].push_back(&g);
+        load[best] += g.cost;
+        count[best] += g.end - g.begin;
+    }
+    const size_t slots = *std::max_element(count.begin(), count.end());
+    out.assign(slots * static_cast<size_t>(n_xcd), LatentItem{});
+    for (int x = 0; x < n_xcd; ++x) {
+        size_t s = 0;
+        for (const Group* g : bins[x])
+            for (size_t i = g->begin; i < g->end; ++i, ++s) out[s * n_xcd + x] = tiles[i].item;
+    }
+    return true;
+}
+
 }  // namespace mla

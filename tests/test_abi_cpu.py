@@ -298,3 +298,82 @@ def test_paged_prefill_rejects_invalid_arguments_before_any_hip_call():
     assert call(pages=0) == 1
     assert call(scale=-1.0) == 1
     assert call(dtype=3) == 2
+
+
+# ---------------------------------------------------------------------------
+# weight-absorbed prefill: work list and argument checks (no HIP call)
+# ---------------------------------------------------------------------------
+
+ABS_BM = 128
+
+
+def _check_latent_plan(qo_lens, kv_lens, heads, causal):
+    qo = np.concatenate([[0], np.cumsum(qo_lens)]).astype(np.int32)
+    kv = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
+    items = mra.absorbed_plan_items(qo, kv, heads, causal)
+    assert len(items) % 8 == 0
+    cover = np.zeros(int(qo[-1]) * heads, dtype=np.int64)
+    groups = {}
+    for i, (row0, n_rows, seq_row0, kv_hi, kv_start, kv_len, diag_base, res) in enumerate(items):
+        if n_rows == 0:
+            assert not np.any(items[i]), "padding items are all zero"
+            continue
+        assert 0 < n_rows <= ABS_BM and res == 0
+        seq = int(np.searchsorted(qo * heads, row0, side="right")) - 1
+        assert seq_row0 == qo[seq] * heads
+        assert (row0 - seq_row0) % ABS_BM == 0
+        assert row0 + n_rows <= qo[seq + 1] * heads        # inside its sequence
+        assert kv_start == kv[seq] and kv_len == kv[seq + 1] - kv[seq]
+        qo_len = qo[seq + 1] - qo[seq]
+        assert diag_base == (kv_len - qo_len if causal else kv_len)
+        last_tok = (row0 + n_rows - 1 - seq_row0) // heads
+        assert kv_hi == min(kv_len, max(0, diag_base + last_tok + 1))
+        cover[row0:row0 + n_rows] += 1
+        groups.setdefault(seq, set()).add(i % 8)
+    assert np.all(cover == 1)
+    return items, groups
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_absorbed_partition_covers_every_row_once(causal):
+    _check_latent_plan([1, 17, 64, 300, 0, 129], [1, 17, 64, 300, 5, 129], 16, causal)
+    _check_latent_plan([5, 300, 0, 7, 513], [2, 0, 9, 40, 513], 3, causal)   # odd H
+    _check_latent_plan([1, 2, 3], [1, 2, 3], 1, causal)
+
+
+def test_absorbed_partition_keeps_short_sequences_on_one_xcd():
+    # at most 256 tiles per group: a sequence with fewer tiles stays on one XCD
+    items, groups = _check_latent_plan([100, 40, 4000, 8], [100, 40, 4000, 8], 16, True)
+    assert len(groups[0]) == 1 and len(groups[1]) == 1 and len(groups[3]) == 1
+    assert len(groups[2]) == 2         # 4000 x 16 rows = 500 tiles: two groups
+
+
+def test_absorbed_prefill_rejects_invalid_arguments_before_any_hip_call():
+    lib = mra.lib()
+    qo = np.array([0, 4], dtype=np.int32)
+    kv = np.array([0, 4], dtype=np.int32)
+    bad_qo = np.array([0, 4, 2], dtype=np.int32)
+    args = lambda **kw: dict(dict(q=16, kv=16, qo=qo.ctypes.data, kvp=kv.ctypes.data, batch=1,
+                                  heads=2, causal=1, scale=0.1, out=16, lse=16), **kw)
+    def call(**kw):
+        a = args(**kw)
+        return lib.mla_absorbed_prefill(a["q"], a["kv"], a["qo"], a["kvp"], a["batch"],
+                                        a["heads"], a["causal"], a["scale"], a["out"], a["lse"],
+                                        None)
+    assert call(scale=0.0) == 1
+    assert call(scale=float("nan")) == 1
+    assert call(heads=0) == 1
+    assert call(causal=2) == 1
+    assert call(batch=-1) == 1
+    assert call(q=None) == 1
+    assert call(kv=None) == 1
+    assert call(out=20) == 1                          # misaligned
+    assert call(qo=bad_qo.ctypes.data, kvp=np.array([0, 1, 2], dtype=np.int32).ctypes.data,
+                batch=2) == 1                         # decreasing indptr
+    assert call(qo=np.array([1, 4], dtype=np.int32).ctypes.data) == 1   # indptr[0] != 0
+    big = np.array([0, 1 << 24], dtype=np.int32)
+    assert call(qo=big.ctypes.data, heads=256) == 1  # tokens x heads >= 2^31
+    # nothing to do: returns before any HIP call
+    empty = np.array([0], dtype=np.int32)
+    assert call(qo=empty.ctypes.data, kvp=empty.ctypes.data, batch=0, q=None, kv=None,
+                out=None, lse=None) == 0

@@ -466,3 +466,70 @@ def test_decompress_then_prefill_full_size():
         ro, rl = oracle.prefill(qh, rk, rv, d.indptr, d.indptr, True, d.sm_scale, rows)
         check(o[idx, h:h + 1].cpu(), lse[idx, h:h + 1].cpu(), ro, rl, torch.bfloat16,
               f"decompress+prefill head {h}")
+
+
+# ---------------------------------------------------------------------------
+# weight-absorbed prefill over the latent cache
+# ---------------------------------------------------------------------------
+
+def _absorbed_parity(x: workloads.AbsorbedInputs, what, rows=None):
+    _flush(f"[gpu] absorbed {what}: Tq={x.qo_indptr[-1]} Tk={x.kv_indptr[-1]} H={x.num_heads} "
+           f"causal={x.causal}")
+    o, lse = mra.absorbed_prefill(x.q.to(DEV), x.kv.to(DEV), x.qo_indptr, x.kv_indptr, x.causal,
+                                  x.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.absorbed(x.q, x.kv, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale,
+                             rows=rows)
+    if rows is not None:
+        idx = torch.tensor(rows)
+        o, lse = o[idx], lse[idx]
+    return check(o, lse, ro, rl, torch.bfloat16, f"absorbed {what}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("heads", [16, 3, 1])
+def test_absorbed_small_parity(causal, heads):
+    # ragged lengths spanning several 32-key tiles and 128-row tiles, with tails
+    lens = [1, 17, 64, 130, 33]
+    x = workloads.absorbed_inputs(lens, lens, heads, seed=11, causal=causal)
+    _absorbed_parity(x, f"lens {lens} H={heads}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_absorbed_context_and_empty_sequences(causal):
+    # kv > qo (a context chunk in front), qo > kv (causal rows with no
+    # visible key), kv = 0, qo = 0
+    qo = [5, 40, 100, 7, 0, 3]
+    kv = [37, 40, 300, 0, 9, 1]
+    x = workloads.absorbed_inputs(qo, kv, 8, seed=12, causal=causal)
+    _absorbed_parity(x, f"qo {qo} kv {kv}")
+
+
+def test_absorbed_many_heads():
+    # 128 heads: one token's rows fill a whole 128-row tile
+    lens = [3, 70, 40]
+    x = workloads.absorbed_inputs(lens, lens, 128, seed=13, causal=True)
+    _absorbed_parity(x, "128 heads")
+
+
+def test_absorbed_scale_extremes():
+    # large scores (rescale path) and tiny ones
+    lens = [200, 90]
+    for scale in (1.0, 1e-3):
+        x = workloads.absorbed_inputs(lens, lens, 4, seed=14, causal=True, sm_scale=scale)
+        _absorbed_parity(x, f"sm_scale {scale}")
+
+
+def test_absorbed_batch_full_size_sampled():
+    x = workloads.absorbed_batch(device=DEV)
+    _flush(f"[gpu] absorbed_batch Tq={x.qo_indptr[-1]} H={x.num_heads}")
+    o, lse = mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    torch.cuda.synchronize()
+    _row_properties(o, lse)
+    rows = sample_rows(x.qo_indptr, block=2048, n_random=24, seed=6)
+    ro, rl = oracle.absorbed(x.q.cpu(), x.kv.cpu(), x.qo_indptr, x.kv_indptr, True, x.sm_scale,
+                             rows=rows)
+    idx = torch.tensor(rows)
+    check(o[idx].cpu(), lse[idx].cpu(), ro, rl, torch.bfloat16, "absorbed_batch sampled rows")
+    del x, o, lse
+    torch.cuda.empty_cache()

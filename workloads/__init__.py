@@ -66,6 +66,19 @@ class ChunkedInputs:
 
 
 @dataclass
+class AbsorbedInputs:
+    """Weight-absorbed MLA over the latent cache: absorbed queries and the
+    shared cache rows (c_kv | k_rope)."""
+    q: torch.Tensor                    # [Tq, H, 576]
+    kv: torch.Tensor                   # [Tk, 576]
+    qo_indptr: List[int]
+    kv_indptr: List[int]
+    num_heads: int
+    causal: bool
+    sm_scale: float
+
+
+@dataclass
 class DecompressInputs:
     c_kv: torch.Tensor                 # [T, 512]
     k_rope: torch.Tensor               # [T, 64]
@@ -216,6 +229,28 @@ def decompress_batch(device="cpu", num_seqs: int = 8, seq_len: int = 4096,
                             default_sm_scale())
 
 
+def absorbed_inputs(lengths_q, lengths_kv, num_heads: int, seed: int, causal: bool = True,
+                    device="cpu", sm_scale: Optional[float] = None) -> AbsorbedInputs:
+    """Absorbed queries q [Tq,H,576] and latent cache rows kv [Tk,576], both
+    N(0,1) rounded to bf16; drawn in that order. The score scale defaults
+    to 1/sqrt(192), the head dim the absorbed scores stand in for."""
+    g = _gen(seed, device)
+    qo = indptr_from_lengths(lengths_q)
+    kv = indptr_from_lengths(lengths_kv)
+    dk = D_LATENT + D_ROPE
+    q = randn((qo[-1], num_heads, dk), g, torch.bfloat16, device)
+    c = randn((kv[-1], dk), g, torch.bfloat16, device)
+    return AbsorbedInputs(q, c, qo, kv, num_heads, causal,
+                          default_sm_scale() if sm_scale is None else sm_scale)
+
+
+def absorbed_batch(device="cpu", num_heads: int = 128) -> AbsorbedInputs:
+    """The DeepSeek-V3 batch lengths (16 seqs U[256,4096], seed 2) through the
+    absorbed path: causal, bf16, seed 6."""
+    lens = deepseek_v3_lengths()
+    return absorbed_inputs(lens, lens, num_heads, seed=6, causal=True, device=device)
+
+
 def merge_inputs(num_tokens: int, num_heads: int, dtype: torch.dtype, seed: int,
                  device="cpu", neg_inf_frac: float = 0.0):
     """Two (O, LSE) partial states. O ~ N(0,1); LSE ~ N(0, 4) so the two weights
@@ -245,4 +280,5 @@ WORKLOADS = {
     "chunked_prefill": "8 x (2048 new causal + 2 x 4096 context non-causal), 128 heads, bf16, merged",
     "skewed_batch": "64 seqs log-uniform [16,32768], total <= 262144, 128 heads, bf16, causal",
     "decompress_batch": "8 x 4096 tokens, latent 512 -> 128 heads via W_UK/W_UV, then causal prefill",
+    "absorbed_batch": "16 seqs U[256,4096] (seed 2), 128 heads, absorbed q [T,H,576] over kv [T,576], bf16, causal",
 }
