@@ -19,10 +19,14 @@
 //  * Each 32-key tile (36 KB: 36 blocks of 8 keys x 64 dims, chunk-swizzled)
 //    is loaded straight into LDS with global_load_lds_dwordx4 and serves both
 //    products: its fragments are the A operand of S^T = K Q^T
-//    (v_mfma_f32_32x32x16_bf16, 36 k-steps, two independent accumulator
-//    chains), and transposing reads (ds_read_b64_tr_b16) of its first 512
-//    dims are the V^T operand of O^T = V^T P^T (16 dv blocks x 2 k-steps).
-//    Every K/V byte in LDS feeds 128 rows.
+//    (v_mfma_f32_32x32x16_bf16, 36 k-steps in one accumulator chain: dependent
+//    MFMAs issue back to back), and transposing reads (ds_read_b64_tr_b16) of
+//    its first 512 dims are the V^T operand of O^T = V^T P^T (16 dv blocks x
+//    2 k-steps). LDS fragments are read four MFMAs ahead of use.
+//  * LDS read bandwidth, not the matrix cores, bounds this kernel: each wave
+//    reads the whole tile (36 KB as 16-byte rows, 32 KB through transposing
+//    reads at about half that rate) for its 32 rows. The chunk swizzle keeps
+//    both read kinds free of bank conflicts on the 64-bank LDS.
 //  * PV is deferred by one tile: iteration j computes the scores of tile j,
 //    then PV of tile j-1 (independent MFMAs) next to the softmax of tile j
 //    (VALU), so one wave alone keeps the matrix cores busy. A tile's stage
@@ -71,8 +75,15 @@ __device__ __forceinline__ float xor32_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// chunk swizzle key of tile row (key) `row`
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// Chunk swizzle of tile row (key) `row`: the 16-byte chunk c of a row sits
+// at slot c ^ swz(row). 128-byte rows, so two rows share one 256-byte bank
+// period. A 16-byte read by 16 lanes (keys of one parity, same chunk) needs
+// swz to be a permutation over those 8 keys; a transposing read by 32 lanes
+// (keys 4i..4i+3, four chunks of one aligned group) needs keys 4i and 4i+2 in
+// different 4-slot halves, hence bit 2 of swz from bit 1 of the key.
+__device__ __forceinline__ int swz(int row) {
+    return ((row >> 1) & 1) << 2 | ((row >> 2) & 1) << 1 | ((row >> 3) & 1);
+}
 
 // One 16-byte-per-lane global -> LDS load (lane l's 16 bytes land at
 // lds_dst + 16 l), issued as inline asm so the compiler does not wait for it
@@ -129,7 +140,7 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     wave_rows = wave_rows < 0 ? 0 : (wave_rows > 32 ? 32 : wave_rows);
     // keys visible to flat row rho: those of its token, rho's token index in
     // the sequence being (rho - seq_row0) / H
-    auto lim_of_row = [&](int r) {
+    auto lim_of_row = [&](int r) __attribute__((always_inline)) {
         const int tok = (it.row0 + r - it.seq_row0) / H;
         int n = it.diag_base + tok + 1;
         n = n < 0 ? 0 : n;
@@ -142,17 +153,15 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
 
     // Q fragments (B operand): this lane's row, dims 16 s + 8 g .. +8; rows
     // past the tile's end load its last row (their results are never stored).
-    // Loaded with inline asm, before the first K/V tile, so the wait for
-    // that tile covers them too and the compiler, which cannot see these
-    // loads, puts no waits of its own on Q inside the key loop (those would
-    // also drain the tiles in flight).
+    // Plain loads, issued after the first two K/V tiles and completed by a
+    // compiler-visible wait before the key loop: the compiler then sees no
+    // Q load in flight and puts no waits of its own inside the loop (those
+    // would also drain the tiles in flight).
     bf16x8_t qf[kKSteps];
+    const bf16x8_t* q_src;
     {
         const int64_t rho = (int64_t)it.row0 + (my_row < it.n_rows ? my_row : it.n_rows - 1);
-        const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(q + rho * kDk) + g;
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s)
-            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[s]) : "v"(src + 2 * s) : "memory");
+        q_src = reinterpret_cast<const bf16x8_t*>(q + rho * kDk) + g;
     }
 
     f32x16_t oacc[kDvBlocks];
@@ -172,7 +181,7 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) ld_col[j] = (uint32_t)(8 * j + ((lane & 7) ^ swz(ld_row))) * 16;
     const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(kv + (int64_t)it.kv_start * kDk);
-    auto issue_tile = [&](int kt, int stage) {
+    auto issue_tile = [&](int kt, int stage) __attribute__((always_inline)) {
         uint8_t* dst = smem + stage * kTileBytes + wave * kGroups * 1024;
         const int key0 = kt * kBN;
         const uint8_t* src = kvseq + (uint64_t)key0 * krow;
@@ -212,16 +221,26 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     }
 
     // ---- compute pieces ----
-    auto scores = [&](int kt, int stage, auto masked, f32x16_t& sacc) {
+    // LDS fragments are read kPre MFMAs ahead of their use: with one wave
+    // per SIMD nothing else hides the LDS latency.
+    constexpr int kPre = 4;
+    auto kfrag = [&](const uint8_t* ks, int s) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8_t*>(ks + k_off[s & 3] + (s >> 2) * 1024);
+    };
+    // S^T of tile kt: one accumulator chain over the 36 k-steps
+    auto scores = [&](int kt, int stage, auto masked, f32x16_t& sacc) __attribute__((always_inline)) {
         constexpr bool kMasked = decltype(masked)::value;
         const uint8_t* ks = smem + stage * kTileBytes;
-        f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};
+        bf16x8_t a[kPre];
+#pragma unroll
+        for (int s = 0; s < kPre; ++s) a[s] = kfrag(ks, s);
+        f32x16_t acc = f32x16_t{};
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + k_off[s & 3] + (s >> 2) * 1024);
-            s2[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s2[s & 1], 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % kPre], qf[s], acc, 0, 0, 0);
+            if (s + kPre < kKSteps) a[s % kPre] = kfrag(ks, s + kPre);
         }
-        sacc = s2[0] + s2[1];
+        sacc = acc;
         if constexpr (kMasked) {
             const int key0 = kt * kBN;
 #pragma unroll
@@ -231,7 +250,8 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
             }
         }
     };
-    auto vfrag = [&](const uint8_t* st, int db, int mm) {
+    auto vfrag = [&](const uint8_t* st, int i) __attribute__((always_inline)) {
+        const int db = i >> 1, mm = i & 1;
         bf16x8_t a;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -245,39 +265,39 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
         }
         return a;
     };
-    auto pv = [&](int stage, const bf16x8_t (&pf)[2]) {
+    // O^T += V^T P^T for the tile in `stage`: 16 dv blocks x 2 key steps
+    constexpr int kPvSteps = kDvBlocks * 2;
+    auto pv = [&](int stage, const bf16x8_t (&pf)[2]) __attribute__((always_inline)) {
         const uint8_t* st = smem + stage * kTileBytes;
+        bf16x8_t a[kPre];
 #pragma unroll
-        for (int db = 0; db < kDvBlocks; ++db) {
+        for (int i = 0; i < kPre; ++i) a[i] = vfrag(st, i);
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm)
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(st, db, mm), pf[mm], oacc[db], 0, 0, 0);
+        for (int i = 0; i < kPvSteps; ++i) {
+            oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kPre], pf[i & 1], oacc[i >> 1], 0, 0, 0);
+            if (i + kPre < kPvSteps) a[i % kPre] = vfrag(st, i + kPre);
         }
     };
-    // max, lazy rescale, p = exp2(s - m) as bf16 and the row sum
-    auto softmax = [&](const f32x16_t& sacc, bf16x8_t (&pf)[2]) {
+    auto tile_max = [&](const f32x16_t& sacc) __attribute__((always_inline)) {
         float mx = sacc[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-        const float mt = xor32_max(mx) * scale_log2;
-        if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            // O is still zero before the first accumulated tile
-            if (m_run != -INFINITY) {
+        return xor32_max(mx) * scale_log2;
+    };
+    // O *= alpha, in place on the accumulators
+    auto scale_o = [&](float alpha) __attribute__((always_inline)) {
 #pragma unroll
-                for (int db = 0; db < kDvBlocks; ++db) {
+        for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float x = oacc[db][i];
-                        agpr_scale(x, alpha);
-                        oacc[db][i] = x;
-                    }
-                }
+            for (int i = 0; i < 16; ++i) {
+                float x = oacc[db][i];
+                agpr_scale(x, alpha);
+                oacc[db][i] = x;
             }
-            m_run = m_new;
-            l_run *= alpha;
         }
+    };
+    // p = exp2(s - m) as bf16, and the row sum of those bf16 values
+    auto exp_part = [&](const f32x16_t& sacc, bf16x8_t (&pf)[2]) __attribute__((always_inline)) {
         const float msub = m_run == -INFINITY ? 0.0f : m_run;
         float lsum = l_run;
 #pragma unroll
@@ -300,29 +320,49 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     // ---- pipeline ----
     // Iteration j: wait for tile j (tile j+1 may still be in flight), barrier
     // (retires tile j-2), issue tile j+2 into tile j-2's stage, scores of
-    // tile j, PV of tile j-1, softmax of tile j.
+    // tile j, then the softmax of tile j (against the new running maximum)
+    // interleaved with PV of tile j-1 (whose P was taken against the old
+    // one), and last, if the maximum moved, O *= 2^(m_old - m_new).
     const int n_tiles = (it.kv_hi + kBN - 1) / kBN;
     const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
     const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
-    auto sync_top = [&](int j) {
+    auto sync_top = [&](int j) __attribute__((always_inline)) {
         if (j + 1 < n_tiles) wait_vmcnt<kLoadsPerTile>();
         else wait_vmcnt<0>();
         __syncthreads();
         if (j + 2 < n_tiles) issue_tile(j + 2, (j + 2) % kStages);
     };
     for (int t = 0; t < 2 && t < n_tiles; ++t) issue_tile(t, t);
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) qf[s] = q_src[2 * s];
+    // s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their maxima): Q and
+    // the first tiles have all landed
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
 
     bf16x8_t pprev[2];
     int j = 0;
-    // iteration kind: 0 = first tile (no PV), 1 = PV of the previous tile;
-    // masked: the scores need the per-row key limit
-    auto iteration = [&](int jj, auto with_pv, auto masked) {
+    auto iteration = [&](int jj, auto with_pv, auto masked) __attribute__((always_inline)) {
+        constexpr bool kPv = decltype(with_pv)::value;
         sync_top(jj);
         f32x16_t sacc;
         scores(jj, jj % kStages, masked, sacc);
-        if constexpr (decltype(with_pv)::value) pv((jj - 1) % kStages, pprev);
+        const float mt = tile_max(sacc);
+        // lazy rescale: the maximum moves only when some row's tile maximum
+        // exceeds it by more than 2^8 (a wave-uniform decision)
+        const bool moved = __any(mt > m_run + kLazyRescale);
+        const float m_new = moved ? fmaxf(m_run, mt) : m_run;
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
         bf16x8_t pcur[2];
-        softmax(sacc, pcur);
+        exp_part(sacc, pcur);
+        if constexpr (kPv) {
+            pv((jj - 1) % kStages, pprev);
+            // keeps the softmax above the rescale branch, in the PV region
+            asm volatile("" ::"v"(pcur[0]), "v"(pcur[1]), "v"(l_run));
+            // O is still zero before the first PV, so only later tiles rescale
+            if (__builtin_expect(moved, 0)) scale_o(alpha);
+        }
         pprev[0] = pcur[0];
         pprev[1] = pcur[1];
     };
