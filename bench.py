@@ -14,7 +14,9 @@ masked work inside partial tiles is not counted).
 
 Also measured in the same run (reported under "secondary"): merge_state at
 the chunked-prefill size (16384 tokens x 128 heads, bf16), against the HBM
-roofline.
+roofline; the device-planned path, the chunked prefill with its merges, the
+paged context pass, a skewed batch, KV decompression followed by prefill,
+and the weight-absorbed prefill over the latent cache.
 
 cpu_baseline: the fp64 oracle (test infrastructure, timed as it stands) on a
 bounded sample of the same workload's (row, head) pairs, on this host's cores.
@@ -94,7 +96,7 @@ def parse():
                     help="target CPU time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
-    ap.add_argument("--only", choices=["merge", "decompress"], default=None,
+    ap.add_argument("--only", choices=["merge", "decompress", "absorbed"], default=None,
                     help="run only one secondary kernel (for profiling) and print its figures")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; "
@@ -370,6 +372,39 @@ def time_decompress(mra, torch, workloads, steps, warmup, with_prefill=True):
     return out
 
 
+def time_absorbed(mra, torch, workloads, steps, warmup):
+    """Weight-absorbed prefill over the latent cache on the DeepSeek-V3 batch
+    lengths: 576-dim absorbed queries, 576-dim shared cache rows, 512-dim
+    values, 128 heads, causal. FLOPs = 2 * heads * visible pairs * (576 + 512)."""
+    x = workloads.absorbed_batch(device="cuda")
+    H = x.num_heads
+    pairs = visible_pairs(x.qo_indptr, x.kv_indptr, x.causal)
+    flops = 2.0 * H * pairs * (576 + 512)
+    out, lse = mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale)
+    for _ in range(warmup):
+        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale,
+                             out=out, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale,
+                             out=out, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = flops / ms / 1e9
+    return {"workload": f"absorbed_batch: DeepSeek-V3 batch lengths, {x.qo_indptr[-1]} tokens, "
+                        f"{H} heads, q [T,H,576] over kv [T,576], Dv 512, causal",
+            "kernel_ms": round(ms, 4), "TFLOP/s": round(tflops, 1), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": profile_traffic(
+                             "prefill_absorbed_deepseek_v3_batch.txt",
+                             "mla_ragged_chunked_amd/csrc/prefill_absorbed.hip"),
+                         "kernel": "prefill_absorbed_kernel"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -393,6 +428,9 @@ def main():
     mra.lib()
     if args.only == "merge":
         print(json.dumps(time_merge(mra, torch, workloads, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "absorbed":
+        print(json.dumps(time_absorbed(mra, torch, workloads, args.steps, args.warmup)), flush=True)
         return
     if args.only == "decompress":
         print(json.dumps(time_decompress(mra, torch, workloads, args.steps, args.warmup,
@@ -465,6 +503,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: decompression + prefill ...")
         sec["decompress_batch"] = time_decompress(mra, torch, workloads, max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
+        log("secondary: absorbed prefill over the latent cache ...")
+        sec["absorbed_batch"] = time_absorbed(mra, torch, workloads, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
         result["secondary"] = sec
     print(json.dumps(result), flush=True)

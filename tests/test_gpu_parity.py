@@ -533,3 +533,12 @@ def test_absorbed_batch_full_size_sampled():
     check(o[idx].cpu(), lse[idx].cpu(), ro, rl, torch.bfloat16, "absorbed_batch sampled rows")
     del x, o, lse
     torch.cuda.empty_cache()
+
+
+def test_absorbed_decode_shape():
+    # one new token per sequence over a prefix (a decode step): each sequence
+    # is a single tile of H rows that visits every key
+    qo = [1, 1, 1, 1]
+    kv = [1000, 37, 2500, 1]
+    x = workloads.absorbed_inputs(qo, kv, 128, seed=15, causal=True)
+    _absorbed_parity(x, "decode shape")
