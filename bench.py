@@ -394,9 +394,40 @@ def time_absorbed(mra, torch, workloads, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     tflops = flops / ms / 1e9
+    # the same rows from a page pool (pages of 64 in a seeded random order)
+    page = 64
+    lens = [b - a for a, b in zip(x.kv_indptr, x.kv_indptr[1:])]
+    per = [-(-n // page) for n in lens]
+    g = torch.Generator().manual_seed(11)
+    perm = torch.randperm(sum(per), generator=g).tolist()
+    pool = torch.empty((sum(per), page, 576), dtype=x.kv.dtype, device="cuda")
+    table = torch.zeros((len(lens), max(per)), dtype=torch.int32)
+    i = 0
+    for b, n in enumerate(lens):
+        for pg in range(per[b]):
+            table[b, pg] = perm[i]
+            m = min(page, n - pg * page)
+            pool[perm[i], :m] = x.kv[x.kv_indptr[b] + pg * page:x.kv_indptr[b] + pg * page + m]
+            i += 1
+    table = table.to("cuda")
+    po, pl = mra.absorbed_prefill_paged(x.q, pool, x.qo_indptr, x.kv_indptr, table, x.causal,
+                                        x.sm_scale)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(po, out) and torch.equal(pl, lse))
+    e0.record()
+    for _ in range(steps):
+        mra.absorbed_prefill_paged(x.q, pool, x.qo_indptr, x.kv_indptr, table, x.causal,
+                                   x.sm_scale, out=po, lse=pl)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_paged = e0.elapsed_time(e1) / steps
+    del pool, po, pl
     return {"workload": f"absorbed_batch: DeepSeek-V3 batch lengths, {x.qo_indptr[-1]} tokens, "
                         f"{H} heads, q [T,H,576] over kv [T,576], Dv 512, causal",
             "kernel_ms": round(ms, 4), "TFLOP/s": round(tflops, 1), "flops": flops,
+            "paged_kernel_ms": round(ms_paged, 4),
+            "paged_TFLOP/s": round(flops / ms_paged / 1e9, 1),
+            "paged_bit_identical": same,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": profile_traffic(

@@ -303,6 +303,29 @@ int mla_absorbed_prefill(const void *q, const void *kv, const int32_t *qo_indptr
                          int32_t causal, float sm_scale, void *out, float *lse, void *stream);
 
 /*
+ * Paged variant of mla_absorbed_prefill: the latent cache rows come from a
+ * page pool through a block table (the absorb path of sglang issue 3849 runs
+ * over a paged prefix held in the token-to-KV pool; block_table as in
+ * "[KVCache] PagedKVCache refactor, FlashInfer JIT and MLA integration").
+ *
+ *   kv_cache     device bf16 [num_pages, page_size, 576].
+ *   block_table  DEVICE int32 [batch, max_pages]: key j of sequence b is slot
+ *                j % page_size of page block_table[b * max_pages + j / page_size].
+ *                Entries outside [0, num_pages) are clamped into the pool (no
+ *                out-of-bounds access; the result is then meaningless).
+ *   page_size    a positive multiple of 32.
+ *   kv_indptr    HOST: only the lengths kv_indptr[b+1] - kv_indptr[b] are used
+ *                (each at most max_pages * page_size).
+ * Everything else is as for mla_absorbed_prefill; for the same cache rows the
+ * outputs are identical bit for bit to the contiguous call.
+ */
+int mla_absorbed_prefill_paged(const void *q, const void *kv_cache, const int32_t *qo_indptr,
+                               const int32_t *kv_indptr, const int32_t *block_table,
+                               int32_t max_pages, int32_t page_size, int32_t num_pages,
+                               int32_t batch, int32_t num_heads, int32_t causal, float sm_scale,
+                               void *out, float *lse, void *stream);
+
+/*
  * Host-only view of the absorbed prefill's work list (no HIP call): writes
  * *n_items and, if dst is non-NULL and capacity_items suffices, the items
  * as 8 int32 each: {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len,

@@ -23,7 +23,7 @@ import numpy as np
 import torch
 
 __all__ = ["ragged_prefill", "ragged_prefill_paged", "merge_state", "decompress_kv",
-           "absorbed_prefill", "absorbed_plan_items", "Plan", "DevicePlan", "MlaError", "lib",
+           "absorbed_prefill", "absorbed_prefill_paged", "absorbed_plan_items", "Plan", "DevicePlan", "MlaError", "lib",
            "LIB_PATH", "DQK", "DVO", "DLAT", "DROPE", "EXPORTED_SYMBOLS"]
 
 DQK, DVO, DLAT, DROPE = 192, 128, 512, 64
@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = [
     "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
     "mla_ragged_prefill_device_plan", "mla_ragged_prefill_paged",
     "mla_merge_state", "mla_decompress_kv", "mla_absorbed_prefill", "mla_absorbed_plan_items",
+    "mla_absorbed_prefill_paged",
 ]
 
 
@@ -90,6 +91,8 @@ def lib():
         "mla_absorbed_prefill": ([P, P, P, P, I32, I32, I32, F, P, P, P], ctypes.c_int),
         "mla_absorbed_plan_items": ([P, P, I32, I32, I32, P, I64, ctypes.POINTER(I64)],
                                     ctypes.c_int),
+        "mla_absorbed_prefill_paged": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, P, P, P],
+                                       ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(l, name)
@@ -450,4 +453,49 @@ def absorbed_prefill(q: torch.Tensor, kv: torch.Tensor, qo_indptr, kv_indptr, ca
                                           _ptr(out), _ptr(lse) if return_lse else None,
                                           _stream(q.device)),
                "mla_absorbed_prefill")
+    return (out, lse) if return_lse else out
+
+
+def absorbed_prefill_paged(q: torch.Tensor, kv_cache: torch.Tensor, qo_indptr, kv_indptr,
+                           block_table: torch.Tensor, causal: bool, sm_scale: float,
+                           return_lse: bool = True, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None):
+    """absorbed_prefill with the latent cache in a page pool kv_cache
+    [num_pages, page_size, 576] (bf16) read through block_table [batch,
+    max_pages] (int32, on the GPU); host indptrs (only the kv lengths are
+    used from kv_indptr)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(kv_cache, "kv_cache")
+    _dev_tensor(block_table, "block_table")
+    if q.dtype != torch.bfloat16 or kv_cache.dtype != torch.bfloat16:
+        raise ValueError("q and kv_cache must be bf16")
+    dk = DLAT + DROPE
+    if q.dim() != 3 or q.shape[2] != dk or kv_cache.dim() != 3 or kv_cache.shape[2] != dk:
+        raise ValueError("q must be [Tq,H,576] and kv_cache [num_pages,page_size,576]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [batch, max_pages]")
+    qo, kvp = _indptr(qo_indptr), _indptr(kv_indptr)
+    if len(qo) != len(kvp) or len(qo) < 1:
+        raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+    if qo[-1] != q.shape[0] or block_table.shape[0] != len(qo) - 1:
+        raise ValueError("indptr / block_table do not match q's tokens or the batch")
+    tq, heads = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((tq, heads, DLAT), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((tq, heads), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, "out")
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (tq, heads, DLAT):
+        raise ValueError("out must be bf16 [Tq,H,512]")
+    if return_lse:
+        _dev_tensor(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (tq, heads):
+            raise ValueError("lse must be fp32 [Tq,H]")
+    with torch.cuda.device(q.device):
+        _check(lib().mla_absorbed_prefill_paged(
+            _ptr(q), _ptr(kv_cache), qo.ctypes.data, kvp.ctypes.data, _ptr(block_table),
+            block_table.shape[1], kv_cache.shape[1], kv_cache.shape[0], len(qo) - 1, heads,
+            int(bool(causal)), float(sm_scale), _ptr(out), _ptr(lse) if return_lse else None,
+            _stream(q.device)),
+            "mla_absorbed_prefill_paged")
     return (out, lse) if return_lse else out

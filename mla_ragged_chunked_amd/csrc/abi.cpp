@@ -300,7 +300,7 @@ std::mutex g_absorbed_mu;
 std::map<std::pair<int, void*>, AbsorbedState*>* g_absorbed = nullptr;
 
 int absorbed_plan(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_heads,
-                  int32_t causal, std::vector<mla::LatentItem>& items) {
+                  int32_t causal, std::vector<mla::LatentItem>& items, bool paged = false) {
     if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
     if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
     if (num_heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
@@ -310,11 +310,57 @@ int absorbed_plan(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t n
     std::string err;
     try {
         if (!mla::build_latent_work_list(qo, kv, batch, num_heads, causal != 0,
-                                         mla::prefill_absorbed_block_m(), 8, items, err))
+                                         mla::prefill_absorbed_block_m(), 8, items, err, paged))
             return fail(MLA_EINVAL, err);
     } catch (const std::bad_alloc&) {
         return fail(MLA_ENOMEM, "host allocation of the work list failed");
     }
+    return MLA_OK;
+}
+
+// One absorbed prefill call (contiguous cache, or a page pool when `pg`).
+int absorbed_call(const void* q, const void* kv, const int32_t* qo_indptr,
+                  const int32_t* kv_indptr, int32_t batch, int32_t num_heads, int32_t causal,
+                  float sm_scale, void* out, float* lse, void* stream, const mla::PagedKv* pg) {
+    if (int s = check_scale(sm_scale)) return s;
+    std::vector<mla::LatentItem> items;
+    if (int s = absorbed_plan(qo_indptr, kv_indptr, batch, num_heads, causal, items, pg != nullptr))
+        return s;
+    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
+    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
+    if (tq > 0 && (q == nullptr || out == nullptr))
+        return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
+    if ((tk > 0 || pg != nullptr) && kv == nullptr)
+        return fail(MLA_EINVAL, "kv must be non-NULL when there are keys");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
+        return fail(MLA_EINVAL, "q, kv, out and lse must be 16-byte aligned");
+    if (items.empty()) return MLA_OK;
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    AbsorbedState* st = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_absorbed_mu);
+        if (g_absorbed == nullptr)
+            g_absorbed = new (std::nothrow) std::map<std::pair<int, void*>, AbsorbedState*>();
+        if (g_absorbed == nullptr) return fail(MLA_ENOMEM, "absorbed plan table");
+        auto key = std::make_pair(dev, stream);
+        auto it = g_absorbed->find(key);
+        if (it == g_absorbed->end()) {
+            st = new (std::nothrow) AbsorbedState();
+            if (st == nullptr) return fail(MLA_ENOMEM, "absorbed plan");
+            (*g_absorbed)[key] = st;
+        } else {
+            st = it->second;
+        }
+    }
+    st->items.swap(items);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int r = st->dwl.upload(st->items, s)) return r;
+    e = mla::launch_prefill_absorbed(st->dwl.dev, static_cast<int64_t>(st->items.size()), q, kv,
+                                     out, lse, num_heads, sm_scale, s, pg);
+    if (e != hipSuccess) return hip_fail(e, "absorbed prefill kernel launch");
     return MLA_OK;
 }
 
@@ -550,44 +596,31 @@ int mla_absorbed_plan_items(const int32_t* qo_indptr, const int32_t* kv_indptr, 
 int mla_absorbed_prefill(const void* q, const void* kv, const int32_t* qo_indptr,
                          const int32_t* kv_indptr, int32_t batch, int32_t num_heads,
                          int32_t causal, float sm_scale, void* out, float* lse, void* stream) {
-    if (int s = check_scale(sm_scale)) return s;
-    std::vector<mla::LatentItem> items;
-    if (int s = absorbed_plan(qo_indptr, kv_indptr, batch, num_heads, causal, items)) return s;
-    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
-    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
-    if (tq > 0 && (q == nullptr || out == nullptr))
-        return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
-    if (tk > 0 && kv == nullptr) return fail(MLA_EINVAL, "kv must be non-NULL when there are keys");
-    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
-        return fail(MLA_EINVAL, "q, kv, out and lse must be 16-byte aligned");
-    if (items.empty()) return MLA_OK;
+    return absorbed_call(q, kv, qo_indptr, kv_indptr, batch, num_heads, causal, sm_scale, out, lse,
+                         stream, nullptr);
+}
 
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    AbsorbedState* st = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_absorbed_mu);
-        if (g_absorbed == nullptr)
-            g_absorbed = new (std::nothrow) std::map<std::pair<int, void*>, AbsorbedState*>();
-        if (g_absorbed == nullptr) return fail(MLA_ENOMEM, "absorbed plan table");
-        auto key = std::make_pair(dev, stream);
-        auto it = g_absorbed->find(key);
-        if (it == g_absorbed->end()) {
-            st = new (std::nothrow) AbsorbedState();
-            if (st == nullptr) return fail(MLA_ENOMEM, "absorbed plan");
-            (*g_absorbed)[key] = st;
-        } else {
-            st = it->second;
+int mla_absorbed_prefill_paged(const void* q, const void* kv_cache, const int32_t* qo_indptr,
+                               const int32_t* kv_indptr, const int32_t* block_table,
+                               int32_t max_pages, int32_t page_size, int32_t num_pages,
+                               int32_t batch, int32_t num_heads, int32_t causal, float sm_scale,
+                               void* out, float* lse, void* stream) {
+    if (page_size < 32 || page_size % 32 != 0)
+        return fail(MLA_EINVAL, "page_size must be a positive multiple of 32");
+    if (max_pages < 1 || num_pages < 1) return fail(MLA_EINVAL, "max_pages and num_pages must be >= 1");
+    if (batch > 0 && (block_table == nullptr ||
+                      (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))
+        return fail(MLA_EINVAL, "block_table must be non-NULL and 4-byte aligned");
+    if (batch > 0 && kv_indptr != nullptr) {
+        for (int32_t b = 0; b < batch; ++b) {
+            const int64_t len = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+            if (len > (int64_t)max_pages * page_size)
+                return fail(MLA_EINVAL, "a sequence's context exceeds max_pages x page_size");
         }
     }
-    st->items.swap(items);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (int r = st->dwl.upload(st->items, s)) return r;
-    e = mla::launch_prefill_absorbed(st->dwl.dev, static_cast<int64_t>(st->items.size()), q, kv,
-                                     out, lse, num_heads, sm_scale, s);
-    if (e != hipSuccess) return hip_fail(e, "absorbed prefill kernel launch");
-    return MLA_OK;
+    const mla::PagedKv pg{block_table, max_pages, page_size, num_pages};
+    return absorbed_call(q, kv_cache, qo_indptr, kv_indptr, batch, num_heads, causal, sm_scale,
+                         out, lse, stream, &pg);
 }
 
 }  // extern "C"

@@ -78,9 +78,11 @@ bool build_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int bat
 
 // Work list of the weight-absorbed prefill (host only): tiles of `block_m`
 // flat rows, grouped and ordered for the XCDs like build_work_list.
+// `kv_start_is_seq` stores the sequence index in kv_start (paged cache).
 bool build_latent_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
                             int num_heads, bool causal, int block_m, int n_xcd,
-                            std::vector<LatentItem>& out, std::string& err);
+                            std::vector<LatentItem>& out, std::string& err,
+                            bool kv_start_is_seq = false);
 int prefill_absorbed_block_m();
 
 // Device-side partitioner (device_plan.hip). The workspace holds, at these
@@ -107,9 +109,12 @@ hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const voi
                                const void* k, const void* v, void* out, float* lse,
                                int num_heads, float sm_scale, hipStream_t stream,
                                const PagedKv* paged = nullptr);
+// `paged` == nullptr: contiguous cache [Tk, 576] (rows from kv_start); else
+// a page pool [num_pages, page_size, 576] (PagedKv with H = 1).
 hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, const void* q,
                                    const void* kv, void* out, float* lse, int num_heads,
-                                   float sm_scale, hipStream_t stream);
+                                   float sm_scale, hipStream_t stream,
+                                   const PagedKv* paged = nullptr);
 hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b,
                         const float* lse_b, void* o, float* lse, int64_t num_rows,
                         int dtype_bf16, hipStream_t stream);

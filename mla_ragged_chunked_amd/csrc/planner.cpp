@@ -150,7 +150,7 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
 // groups are dealt and laid out exactly as above.
 bool build_latent_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_heads,
                             bool causal, int block_m, int n_xcd, std::vector<LatentItem>& out,
-                            std::string& err) {
+                            std::string& err, bool kv_start_is_seq) {
     constexpr size_t kLatentGroupTiles = 256;
     out.clear();
     if (batch < 0) { err = "batch must be >= 0"; return false; }
@@ -188,7 +188,7 @@ bool build_latent_work_list(const int32_t* qo, const int32_t* kv, int batch, int
             const int64_t last_tok = (r0 + t.item.n_rows - 1) / num_heads;
             const int64_t lim_last = static_cast<int64_t>(diag_base) + last_tok + 1;
             t.item.kv_hi = static_cast<int32_t>(std::min<int64_t>(kv_len, std::max<int64_t>(0, lim_last)));
-            t.item.kv_start = kv[b];
+            t.item.kv_start = kv_start_is_seq ? b : kv[b];
             t.item.kv_len = kv_len;
             t.item.diag_base = diag_base;
             t.item.reserved = 0;

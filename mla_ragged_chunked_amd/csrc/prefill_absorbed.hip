@@ -120,10 +120,14 @@ __device__ __forceinline__ void agpr_scale(float& x, float alpha) {
                  : "v"(alpha));
 }
 
+// kPaged: the cache is a page pool [num_pages, page_size, 576] read through
+// a block table, and LatentItem::kv_start holds the sequence index.
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_t* __restrict__ q,
                              const uint16_t* __restrict__ kv, uint16_t* __restrict__ out,
-                             float* __restrict__ lse, int num_heads, float scale_log2) {
+                             float* __restrict__ lse, int num_heads, float scale_log2, PagedKv pg,
+                             const int32_t* __restrict__ block_table) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
 
     const LatentItem it = items[blockIdx.x];
@@ -180,11 +184,24 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     uint32_t ld_col[kGroups];
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) ld_col[j] = (uint32_t)(8 * j + ((lane & 7) ^ swz(ld_row))) * 16;
-    const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(kv + (int64_t)it.kv_start * kDk);
-    auto issue_tile = [&](int kt, int stage) __attribute__((always_inline)) {
+    const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(kv + (kPaged ? 0 : (int64_t)it.kv_start * kDk));
+    // Table entry of key tile kt (paged cache). The block table is a kernel
+    // argument of its own, __restrict__, so this is a scalar load, which does
+    // not count against the DMA waits; the raw value is clamped into the pool
+    // only where it is used, one issue later, so its latency is not waited for.
+    auto page_entry = [&](int kt) __attribute__((always_inline)) {
+        return block_table[(int64_t)it.kv_start * pg.max_pages + (kt * kBN) / pg.page_size];
+    };
+    // tile kt into `stage` (`entry`: its table entry, paged cache only)
+    auto issue_tile = [&](int kt, int stage, int entry) __attribute__((always_inline)) {
         uint8_t* dst = smem + stage * kTileBytes + wave * kGroups * 1024;
         const int key0 = kt * kBN;
-        const uint8_t* src = kvseq + (uint64_t)key0 * krow;
+        uint64_t row0 = (uint64_t)key0;
+        if constexpr (kPaged) {
+            const int page = entry < 0 ? 0 : (entry >= pg.num_pages ? pg.num_pages - 1 : entry);
+            row0 = (uint64_t)page * pg.page_size + (uint64_t)(key0 % pg.page_size);
+        }
+        const uint8_t* src = kvseq + row0 * krow;
         int r = ld_row;
         if (key0 + kBN - 1 > last_key) r = r < last_key - key0 ? r : last_key - key0;
         const uint32_t roff = (uint32_t)r * krow;
@@ -326,13 +343,25 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     const int n_tiles = (it.kv_hi + kBN - 1) / kBN;
     const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
     const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
+    // tiles are issued in order; with a paged cache the next tile's table
+    // entry is read one issue ahead
+    int iss_page = 0;
+    if constexpr (kPaged) {
+        if (n_tiles > 0) iss_page = page_entry(0);
+    }
+    auto issue_next = [&](int kt) __attribute__((always_inline)) {
+        issue_tile(kt, kt % kStages, iss_page);
+        if constexpr (kPaged) {
+            if (kt + 1 < n_tiles) iss_page = page_entry(kt + 1);
+        }
+    };
     auto sync_top = [&](int j) __attribute__((always_inline)) {
         if (j + 1 < n_tiles) wait_vmcnt<kLoadsPerTile>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (j + 2 < n_tiles) issue_tile(j + 2, (j + 2) % kStages);
+        if (j + 2 < n_tiles) issue_next(j + 2);
     };
-    for (int t = 0; t < 2 && t < n_tiles; ++t) issue_tile(t, t);
+    for (int t = 0; t < 2 && t < n_tiles; ++t) issue_next(t);
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) qf[s] = q_src[2 * s];
     // s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their maxima): Q and
@@ -406,13 +435,21 @@ int prefill_absorbed_block_m() { return kBM; }
 
 hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, const void* q,
                                    const void* kv, void* out, float* lse, int num_heads,
-                                   float sm_scale, hipStream_t stream) {
+                                   float sm_scale, hipStream_t stream, const PagedKv* paged) {
     if (n_items <= 0) return hipSuccess;
     if (n_items > 0x7fffffff) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(prefill_absorbed_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, stream,
-                       items, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
-                       static_cast<uint16_t*>(out), lse, num_heads, scale_log2);
+    const PagedKv pg = paged != nullptr ? *paged : PagedKv{nullptr, 0, 0, 0};
+    if (paged != nullptr)
+        hipLaunchKernelGGL(prefill_absorbed_kernel<true>, dim3((unsigned)n_items), dim3(kThreads), 0,
+                           stream, items, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(kv), static_cast<uint16_t*>(out), lse,
+                           num_heads, scale_log2, pg, pg.block_table);
+    else
+        hipLaunchKernelGGL(prefill_absorbed_kernel<false>, dim3((unsigned)n_items), dim3(kThreads), 0,
+                           stream, items, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(kv), static_cast<uint16_t*>(out), lse,
+                           num_heads, scale_log2, pg, nullptr);
     return hipGetLastError();
 }
 

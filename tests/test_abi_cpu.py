@@ -377,3 +377,22 @@ def test_absorbed_prefill_rejects_invalid_arguments_before_any_hip_call():
     empty = np.array([0], dtype=np.int32)
     assert call(qo=empty.ctypes.data, kvp=empty.ctypes.data, batch=0, q=None, kv=None,
                 out=None, lse=None) == 0
+
+
+def test_absorbed_paged_rejects_invalid_arguments_before_any_hip_call():
+    lib = mra.lib()
+    qo = np.array([0, 4], dtype=np.int32)
+    kv = np.array([0, 64], dtype=np.int32)
+    bt = np.zeros(4, dtype=np.int32)
+
+    def call(page_size=32, max_pages=2, num_pages=4, table=bt.ctypes.data, kvp=kv):
+        return lib.mla_absorbed_prefill_paged(16, 16, qo.ctypes.data, kvp.ctypes.data, table,
+                                              max_pages, page_size, num_pages, 1, 2, 1, 0.1,
+                                              16, 16, None)
+    assert call(page_size=48) == 1                    # not a multiple of 32
+    assert call(page_size=0) == 1
+    assert call(max_pages=0) == 1
+    assert call(num_pages=0) == 1
+    assert call(table=None) == 1
+    assert call(table=bt.ctypes.data + 2) == 1        # misaligned table
+    assert call(kvp=np.array([0, 65], dtype=np.int32)) == 1   # context > max_pages x page_size

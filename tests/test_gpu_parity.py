@@ -542,3 +542,57 @@ def test_absorbed_decode_shape():
     kv = [1000, 37, 2500, 1]
     x = workloads.absorbed_inputs(qo, kv, 128, seed=15, causal=True)
     _absorbed_parity(x, "decode shape")
+
+
+def _latent_paged_cache(x: workloads.AbsorbedInputs, page: int, extra_pages: int, seed: int):
+    """Scatter the contiguous latent cache rows of `x` into a page pool in a
+    random page order (unused slots and pages hold finite filler) and return
+    the pool and the block table (host tensors)."""
+    g = torch.Generator().manual_seed(seed)
+    lens = [b - a for a, b in zip(x.kv_indptr, x.kv_indptr[1:])]
+    per = [-(-n // page) for n in lens]
+    total = sum(per) + extra_pages
+    perm = torch.randperm(total, generator=g).tolist()
+    pool = workloads.randn((total, page, 576), g, torch.bfloat16, "cpu")
+    table = torch.full((len(lens), max(max(per), 1)), -1, dtype=torch.int32)
+    kv_host = x.kv.cpu()
+    i = 0
+    for b, n in enumerate(lens):
+        for pg in range(per[b]):
+            phys = perm[i]
+            i += 1
+            table[b, pg] = phys
+            a = x.kv_indptr[b] + pg * page
+            m = min(page, n - pg * page)
+            pool[phys, :m] = kv_host[a:a + m]
+    return pool, table
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("page", [32, 64, 128])
+def test_absorbed_paged_matches_contiguous(causal, page):
+    qo_lens = [5, 30, 0, 7, 130, 1]
+    kv_lens = [2, 0, 9, 40, 513, 300]
+    x = workloads.absorbed_inputs(qo_lens, kv_lens, 16, seed=47, causal=causal)
+    _flush(f"[gpu] absorbed paged page={page} causal={causal}")
+    pool, table = _latent_paged_cache(x, page, extra_pages=5, seed=page)
+    q, kv = x.q.to(DEV), x.kv.to(DEV)
+    ref_o, ref_l = mra.absorbed_prefill(q, kv, x.qo_indptr, x.kv_indptr, causal, x.sm_scale)
+    o, l = mra.absorbed_prefill_paged(q, pool.to(DEV), x.qo_indptr, x.kv_indptr, table.to(DEV),
+                                      causal, x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_absorbed_paged_prefix_against_the_oracle():
+    # new tokens over a paged prefix (causal, bottom-right), checked directly
+    # against the oracle on the contiguous bytes
+    qo_lens, kv_lens = [64, 1, 9], [200, 96, 257]
+    x = workloads.absorbed_inputs(qo_lens, kv_lens, 8, seed=48, causal=True)
+    _flush("[gpu] absorbed paged prefix vs oracle")
+    pool, table = _latent_paged_cache(x, 64, extra_pages=3, seed=9)
+    o, l = mra.absorbed_prefill_paged(x.q.to(DEV), pool.to(DEV), x.qo_indptr, x.kv_indptr,
+                                      table.to(DEV), True, x.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.absorbed(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    check(o, l, ro, rl, torch.bfloat16, "absorbed paged prefix")
