@@ -96,7 +96,7 @@ def parse():
                     help="target CPU time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
-    ap.add_argument("--only", choices=["merge", "decompress", "absorbed"], default=None,
+    ap.add_argument("--only", choices=["merge", "decompress", "absorbed", "decode"], default=None,
                     help="run only one secondary kernel (for profiling) and print its figures")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; "
@@ -436,6 +436,42 @@ def time_absorbed(mra, torch, workloads, steps, warmup):
                          "kernel": "prefill_absorbed_kernel"}}
 
 
+def time_absorbed_decode(mra, torch, workloads, steps, warmup, batch=64, prefix=4096):
+    """One decode step through the absorbed path: `batch` requests, one new
+    token each, over `prefix`-token latent caches, 128 heads. Each cache row is
+    read once for all heads, so at this size the step is bound by HBM reads
+    of the cache (algorithmic bytes: q, kv, out, lse once)."""
+    x = workloads.absorbed_inputs([1] * batch, [prefix] * batch, 128, seed=53, causal=True,
+                                  device="cuda")
+    H = x.num_heads
+    pairs = visible_pairs(x.qo_indptr, x.kv_indptr, x.causal)
+    flops = 2.0 * H * pairs * (576 + 512)
+    nbytes = 2.0 * (batch * H * 576 + batch * prefix * 576 + batch * H * 512) + 4.0 * batch * H
+    items = mra.absorbed_plan_items(x.qo_indptr, x.kv_indptr, H, True)
+    splits = int(items[:, 8].max()) + 1 if len(items) else 1
+    out, lse = mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    for _ in range(warmup):
+        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale, out=out,
+                             lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale, out=out,
+                             lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = nbytes / ms / 1e6
+    return {"workload": f"absorbed decode: {batch} requests x 1 token over {prefix}-token latent "
+                        f"caches, {H} heads, bf16",
+            "step_ms": round(ms, 4), "kv_splits": splits,
+            "TFLOP/s": round(flops / ms / 1e9, 1), "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "note": "step = absorbed kernel + KV-split merge, both kernels"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -459,6 +495,10 @@ def main():
     mra.lib()
     if args.only == "merge":
         print(json.dumps(time_merge(mra, torch, workloads, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "decode":
+        print(json.dumps(time_absorbed_decode(mra, torch, workloads, args.steps, args.warmup)),
+              flush=True)
         return
     if args.only == "absorbed":
         print(json.dumps(time_absorbed(mra, torch, workloads, args.steps, args.warmup)), flush=True)
@@ -537,6 +577,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: absorbed prefill over the latent cache ...")
         sec["absorbed_batch"] = time_absorbed(mra, torch, workloads, max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
+        log("secondary: absorbed decode step ...")
+        sec["absorbed_decode"] = time_absorbed_decode(mra, torch, workloads, args.steps, 2)
         torch.cuda.empty_cache()
         result["secondary"] = sec
     print(json.dumps(result), flush=True)

@@ -296,7 +296,11 @@ int mla_decompress_kv(const void *c_kv, const void *k_rope, const void *w_uk, co
  *   All device pointers 16-byte aligned. The call plans on the host (the
  *   work list is kept per (device, stream) and reused) and enqueues one
  *   kernel on `stream`; it returns before the kernel ends. Calls on one
- *   stream must come from one thread at a time.
+ *   stream must come from one thread at a time. When the row tiles alone
+ *   cannot fill the GPU (e.g. a decode step, one token per sequence), the
+ *   keys of each tile are split over up to 8 work items (flash-decoding
+ *   style); their fp32 partial states go to a library-owned, grow-only
+ *   buffer per (device, stream) and a second kernel merges them.
  */
 int mla_absorbed_prefill(const void *q, const void *kv, const int32_t *qo_indptr,
                          const int32_t *kv_indptr, int32_t batch, int32_t num_heads,
@@ -328,8 +332,12 @@ int mla_absorbed_prefill_paged(const void *q, const void *kv_cache, const int32_
 /*
  * Host-only view of the absorbed prefill's work list (no HIP call): writes
  * *n_items and, if dst is non-NULL and capacity_items suffices, the items
- * as 8 int32 each: {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len,
- * diag_base, 0}, flat row = token * H + head; n_rows = 0 marks padding.
+ * as 12 int32 each: {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len,
+ * diag_base, kv_lo, part, 0, 0, 0}, flat row = token * H + head, the item's
+ * keys [kv_lo, kv_hi); n_rows = 0 marks padding. part = -1 when the call
+ * writes the output directly; when a call has too few row tiles to fill the
+ * GPU (decode), each tile's keys are split over several items (part = the
+ * split index) whose partial states a second kernel merges.
  */
 int mla_absorbed_plan_items(const int32_t *qo_indptr, const int32_t *kv_indptr, int32_t batch,
                             int32_t num_heads, int32_t causal, int32_t *dst,

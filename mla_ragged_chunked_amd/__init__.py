@@ -398,8 +398,9 @@ def decompress_kv(c_kv: torch.Tensor, k_rope: torch.Tensor, w_uk: torch.Tensor,
 
 
 def absorbed_plan_items(qo_indptr, kv_indptr, num_heads: int, causal: bool) -> np.ndarray:
-    """Host work list of the absorbed prefill: int32 [n_items, 8] rows
-    {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len, diag_base, 0}."""
+    """Host work list of the absorbed prefill: int32 [n_items, 12] rows
+    {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len, diag_base, kv_lo, part,
+    0, 0, 0} (part >= 0: a KV split of its tile)."""
     qo, kv = _indptr(qo_indptr), _indptr(kv_indptr)
     if len(qo) != len(kv) or len(qo) < 1:
         raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
@@ -408,7 +409,7 @@ def absorbed_plan_items(qo_indptr, kv_indptr, num_heads: int, causal: bool) -> n
     _check(l.mla_absorbed_plan_items(qo.ctypes.data, kv.ctypes.data, len(qo) - 1, int(num_heads),
                                      int(bool(causal)), None, 0, ctypes.byref(n)),
            "mla_absorbed_plan_items")
-    buf = np.zeros((max(n.value, 1), 8), dtype=np.int32)
+    buf = np.zeros((max(n.value, 1), 12), dtype=np.int32)
     _check(l.mla_absorbed_plan_items(qo.ctypes.data, kv.ctypes.data, len(qo) - 1, int(num_heads),
                                      int(bool(causal)), buf.ctypes.data, buf.shape[0],
                                      ctypes.byref(n)),

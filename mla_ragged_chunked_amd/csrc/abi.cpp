@@ -295,12 +295,17 @@ int oneshot(const void* q, const void* k, const void* v, const int32_t* qo_indpt
 struct AbsorbedState {
     std::vector<mla::LatentItem> items;
     DeviceWorkList<mla::LatentItem> dwl;
+    // fp32 partial states of KV splits (grow-only; only this stream uses it)
+    void* part = nullptr;
+    size_t part_bytes = 0;
+    int part_device = -1;
 };
 std::mutex g_absorbed_mu;
 std::map<std::pair<int, void*>, AbsorbedState*>* g_absorbed = nullptr;
 
 int absorbed_plan(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_heads,
-                  int32_t causal, std::vector<mla::LatentItem>& items, bool paged = false) {
+                  int32_t causal, std::vector<mla::LatentItem>& items, bool paged = false,
+                  int* splits_out = nullptr) {
     if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
     if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
     if (num_heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
@@ -308,9 +313,19 @@ int absorbed_plan(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t n
     if (batch > 0 && static_cast<int64_t>(kv[batch]) * (MLA_LATENT_DIM + MLA_ROPE_DIM) > INT64_C(1) << 40)
         return fail(MLA_EUNSUPPORTED, "latent cache too large");
     std::string err;
+    int splits = 1;
+    if (batch > 0 && qo[0] == 0 && kv[0] == 0)
+        splits = mla::latent_kv_splits(qo, kv, batch, num_heads, causal != 0,
+                                       mla::prefill_absorbed_block_m());
+    // the partial states of the splits stay below 1 GiB
+    const int64_t rows = batch > 0 ? static_cast<int64_t>(qo[batch]) * num_heads : 0;
+    while (splits > 1 && static_cast<int64_t>(splits) * rows * (MLA_LATENT_DIM + 1) * 4 > (INT64_C(1) << 30))
+        --splits;
+    if (splits_out != nullptr) *splits_out = splits;
     try {
         if (!mla::build_latent_work_list(qo, kv, batch, num_heads, causal != 0,
-                                         mla::prefill_absorbed_block_m(), 8, items, err, paged))
+                                         mla::prefill_absorbed_block_m(), 8, items, err, paged,
+                                         splits))
             return fail(MLA_EINVAL, err);
     } catch (const std::bad_alloc&) {
         return fail(MLA_ENOMEM, "host allocation of the work list failed");
@@ -324,7 +339,9 @@ int absorbed_call(const void* q, const void* kv, const int32_t* qo_indptr,
                   float sm_scale, void* out, float* lse, void* stream, const mla::PagedKv* pg) {
     if (int s = check_scale(sm_scale)) return s;
     std::vector<mla::LatentItem> items;
-    if (int s = absorbed_plan(qo_indptr, kv_indptr, batch, num_heads, causal, items, pg != nullptr))
+    int splits = 1;
+    if (int s = absorbed_plan(qo_indptr, kv_indptr, batch, num_heads, causal, items, pg != nullptr,
+                              &splits))
         return s;
     const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
     const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
@@ -357,10 +374,42 @@ int absorbed_call(const void* q, const void* kv, const int32_t* qo_indptr,
     }
     st->items.swap(items);
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t rows = tq * num_heads;
+    float* part_o = nullptr;
+    float* part_lse = nullptr;
+    if (splits > 1) {
+        const size_t need = static_cast<size_t>(splits) * static_cast<size_t>(rows) *
+                            (MLA_LATENT_DIM + 1) * sizeof(float);
+        if (st->part != nullptr && (st->part_bytes < need || st->part_device != dev)) {
+            // the previous call on this stream may still be using it
+            if (st->part_device == dev) {
+                e = hipStreamSynchronize(s);
+                if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            }
+            (void)hipFree(st->part);
+            st->part = nullptr;
+            st->part_bytes = 0;
+        }
+        if (st->part == nullptr) {
+            e = hipMalloc(&st->part, need);
+            if (e != hipSuccess) {
+                st->part = nullptr;
+                return fail(MLA_ENOMEM, "hipMalloc of the KV-split partial states failed");
+            }
+            st->part_bytes = need;
+            st->part_device = dev;
+        }
+        part_o = static_cast<float*>(st->part);
+        part_lse = part_o + static_cast<size_t>(splits) * rows * MLA_LATENT_DIM;
+    }
     if (int r = st->dwl.upload(st->items, s)) return r;
     e = mla::launch_prefill_absorbed(st->dwl.dev, static_cast<int64_t>(st->items.size()), q, kv,
-                                     out, lse, num_heads, sm_scale, s, pg);
+                                     out, lse, num_heads, sm_scale, s, pg, part_o, part_lse, rows);
     if (e != hipSuccess) return hip_fail(e, "absorbed prefill kernel launch");
+    if (splits > 1) {
+        e = mla::launch_merge_splits(part_o, part_lse, splits, rows, out, lse, s);
+        if (e != hipSuccess) return hip_fail(e, "KV-split merge kernel launch");
+    }
     return MLA_OK;
 }
 
@@ -590,6 +639,7 @@ int mla_absorbed_plan_items(const int32_t* qo_indptr, const int32_t* kv_indptr, 
     if (capacity_items < static_cast<int64_t>(items.size()))
         return fail(MLA_EINVAL, "capacity too small for the work list");
     if (!items.empty()) std::memcpy(dst, items.data(), items.size() * sizeof(mla::LatentItem));
+    static_assert(sizeof(mla::LatentItem) == 12 * sizeof(int32_t), "12 int32 per item");
     return MLA_OK;
 }
 

@@ -46,20 +46,26 @@ struct PagedKv {
 
 // One work item of the weight-absorbed (latent-cache) prefill: a tile of
 // consecutive flat query rows of one sequence, flat row rho = token * H +
-// head. Row rho sees keys [0, lim(rho)) of its sequence,
+// head, over the keys [kv_lo, kv_hi) of that sequence. Row rho sees keys
+// [0, lim(rho)) of its sequence,
 //   lim(rho) = min(kv_len, max(0, diag_base + (rho - seq_row0) / H + 1)),
-// diag_base = kv_len - qo_len when causal, kv_len otherwise. 32 bytes.
+// diag_base = kv_len - qo_len when causal, kv_len otherwise. When the keys of
+// a tile are split over several items (KV splits), each writes a partial
+// (O, LSE) over its keys into split slot `part` and a merge combines them.
+// 48 bytes.
 struct LatentItem {
     int32_t row0;       // first flat row of the tile
     int32_t n_rows;     // rows in the tile; 0 = padding item (kernel returns)
     int32_t seq_row0;   // flat row of the sequence's first token, head 0
-    int32_t kv_hi;      // lim of the tile's last row: keys the tile visits
+    int32_t kv_hi;      // end of the item's keys (at most lim of the tile's last row)
     int32_t kv_start;   // global token index of the sequence's first key
     int32_t kv_len;
     int32_t diag_base;
-    int32_t reserved;
+    int32_t kv_lo;      // first key of the item, a multiple of 32
+    int32_t part;       // -1: final output; else the KV split slot of the partial
+    int32_t pad[3];
 };
-static_assert(sizeof(LatentItem) == 32, "latent work item layout");
+static_assert(sizeof(LatentItem) == 48, "latent work item layout");
 
 // Query-tile heights of the two prefill kernels (each kernel file owns its
 // tile shape; the planner asks for it).
@@ -79,10 +85,16 @@ bool build_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int bat
 // Work list of the weight-absorbed prefill (host only): tiles of `block_m`
 // flat rows, grouped and ordered for the XCDs like build_work_list.
 // `kv_start_is_seq` stores the sequence index in kv_start (paged cache).
+// `splits` >= 1: the keys of every tile are cut into that many item ranges
+// of whole 32-key tiles (1 = no split, items write the final output).
 bool build_latent_work_list(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
                             int num_heads, bool causal, int block_m, int n_xcd,
                             std::vector<LatentItem>& out, std::string& err,
-                            bool kv_start_is_seq = false);
+                            bool kv_start_is_seq = false, int splits = 1);
+// KV splits chosen for a call: more than one only when the row tiles alone
+// cannot fill the chip and the keys are long enough to share out.
+int latent_kv_splits(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                     int num_heads, bool causal, int block_m);
 int prefill_absorbed_block_m();
 
 // Device-side partitioner (device_plan.hip). The workspace holds, at these
@@ -111,10 +123,17 @@ hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const voi
                                const PagedKv* paged = nullptr);
 // `paged` == nullptr: contiguous cache [Tk, 576] (rows from kv_start); else
 // a page pool [num_pages, page_size, 576] (PagedKv with H = 1).
+// Items with part >= 0 write fp32 partials: O to part_o[(part * part_rows
+// + rho) * 512], LSE to part_lse[part * part_rows + rho].
 hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, const void* q,
                                    const void* kv, void* out, float* lse, int num_heads,
                                    float sm_scale, hipStream_t stream,
-                                   const PagedKv* paged = nullptr);
+                                   const PagedKv* paged = nullptr, float* part_o = nullptr,
+                                   float* part_lse = nullptr, int64_t part_rows = 0);
+// Combine `splits` partial states per row into out (bf16 [rows, 512]) and lse
+// (fp32 [rows], may be NULL).
+hipError_t launch_merge_splits(const float* part_o, const float* part_lse, int splits,
+                               int64_t rows, void* out, float* lse, hipStream_t stream);
 hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b,
                         const float* lse_b, void* o, float* lse, int64_t num_rows,
                         int dtype_bf16, hipStream_t stream);

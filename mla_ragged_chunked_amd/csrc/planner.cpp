@@ -147,16 +147,49 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
 // tiles of block_m rows. Groups are runs of at most kLatentGroupTiles
 // consecutive tiles of one sequence (heaviest tiles first), so a long
 // sequence spreads over several XCDs while each group still shares one L2;
-// groups are dealt and laid out exactly as above.
+// groups are dealt and laid out exactly as above. With KV splits every tile
+// becomes `splits` items over consecutive ranges of its 32-key tiles.
+namespace {
+constexpr int kLatentKeyTile = 32;
+}  // namespace
+
+int latent_kv_splits(const int32_t* qo, const int32_t* kv, int batch, int num_heads, bool causal,
+                     int block_m) {
+    // enough items for every CU twice over means no split; otherwise split
+    // up to 8 ways while each split keeps at least 4 key tiles
+    constexpr int64_t kTargetItems = 1024;
+    constexpr int kMaxSplits = 8, kMinTilesPerSplit = 4;
+    if (batch <= 0 || qo == nullptr || kv == nullptr || num_heads < 1 || block_m < 1) return 1;
+    int64_t row_tiles = 0, max_key_tiles = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t qo_len = qo[b + 1] - qo[b], kv_len = kv[b + 1] - kv[b];
+        if (qo_len <= 0 || kv_len <= 0) continue;
+        row_tiles += (qo_len * num_heads + block_m - 1) / block_m;
+        // the last row of the sequence sees the most keys
+        const int64_t diag = causal ? kv_len - qo_len : kv_len;
+        int64_t lim = diag + qo_len;
+        lim = lim < 0 ? 0 : (lim > kv_len ? kv_len : lim);
+        const int64_t t = (lim + kLatentKeyTile - 1) / kLatentKeyTile;
+        max_key_tiles = t > max_key_tiles ? t : max_key_tiles;
+    }
+    if (row_tiles == 0 || row_tiles * 2 >= kTargetItems) return 1;
+    int64_t s = (kTargetItems + row_tiles - 1) / row_tiles;
+    s = s > kMaxSplits ? kMaxSplits : s;
+    const int64_t by_len = max_key_tiles / kMinTilesPerSplit;
+    s = s > by_len ? by_len : s;
+    return s < 1 ? 1 : static_cast<int>(s);
+}
+
 bool build_latent_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_heads,
                             bool causal, int block_m, int n_xcd, std::vector<LatentItem>& out,
-                            std::string& err, bool kv_start_is_seq) {
+                            std::string& err, bool kv_start_is_seq, int splits) {
     constexpr size_t kLatentGroupTiles = 256;
     out.clear();
     if (batch < 0) { err = "batch must be >= 0"; return false; }
     if (num_heads < 1 || num_heads > 65535) { err = "num_heads must be in [1, 65535]"; return false; }
     if (block_m < 1) { err = "block_m must be >= 1"; return false; }
     if (n_xcd < 1 || n_xcd > 64) { err = "n_xcd must be in [1, 64]"; return false; }
+    if (splits < 1 || splits > 64) { err = "splits must be in [1, 64]"; return false; }
     if (batch == 0) return true;
     if (qo == nullptr || kv == nullptr) { err = "indptr pointer is NULL"; return false; }
     if (qo[0] != 0 || kv[0] != 0) { err = "indptr[0] must be 0"; return false; }
@@ -181,19 +214,28 @@ bool build_latent_work_list(const int32_t* qo, const int32_t* kv, int batch, int
         const int32_t diag_base = causal ? kv_len - qo_len : kv_len;
         const size_t begin = tiles.size();
         for (int32_t r0 = 0; r0 < n_rows_seq; r0 += block_m) {
-            LTile t;
+            LTile t{};
             t.item.row0 = seq_row0 + r0;
             t.item.n_rows = std::min(block_m, n_rows_seq - r0);
             t.item.seq_row0 = seq_row0;
             const int64_t last_tok = (r0 + t.item.n_rows - 1) / num_heads;
             const int64_t lim_last = static_cast<int64_t>(diag_base) + last_tok + 1;
-            t.item.kv_hi = static_cast<int32_t>(std::min<int64_t>(kv_len, std::max<int64_t>(0, lim_last)));
+            const int32_t kv_hi =
+                static_cast<int32_t>(std::min<int64_t>(kv_len, std::max<int64_t>(0, lim_last)));
             t.item.kv_start = kv_start_is_seq ? b : kv[b];
             t.item.kv_len = kv_len;
             t.item.diag_base = diag_base;
-            t.item.reserved = 0;
-            t.cost = t.item.kv_hi + kTileFixedCost;
-            tiles.push_back(t);
+            const int32_t key_tiles = (kv_hi + kLatentKeyTile - 1) / kLatentKeyTile;
+            for (int s = 0; s < splits; ++s) {
+                const int32_t t0 = static_cast<int32_t>(static_cast<int64_t>(key_tiles) * s / splits);
+                const int32_t t1 = static_cast<int32_t>(static_cast<int64_t>(key_tiles) * (s + 1) / splits);
+                t.item.kv_lo = t0 * kLatentKeyTile;
+                t.item.kv_hi = s + 1 == splits ? kv_hi : std::min(kv_hi, t1 * kLatentKeyTile);
+                if (t.item.kv_hi < t.item.kv_lo) t.item.kv_hi = t.item.kv_lo;
+                t.item.part = splits > 1 ? s : -1;
+                t.cost = (t.item.kv_hi - t.item.kv_lo) + kTileFixedCost;
+                tiles.push_back(t);
+            }
         }
         std::stable_sort(tiles.begin() + begin, tiles.end(),
                          [](const LTile& a, const LTile& c) { return a.cost > c.cost; });

@@ -49,6 +49,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kDk = kDlat + kDrope;                 // 576
@@ -127,7 +128,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_t* __restrict__ q,
                              const uint16_t* __restrict__ kv, uint16_t* __restrict__ out,
                              float* __restrict__ lse, int num_heads, float scale_log2, PagedKv pg,
-                             const int32_t* __restrict__ block_table) {
+                             const int32_t* __restrict__ block_table, float* __restrict__ part_o,
+                             float* __restrict__ part_lse, int64_t part_rows) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
 
     const LatentItem it = items[blockIdx.x];
@@ -190,12 +192,12 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     // not count against the DMA waits; the raw value is clamped into the pool
     // only where it is used, one issue later, so its latency is not waited for.
     auto page_entry = [&](int kt) __attribute__((always_inline)) {
-        return block_table[(int64_t)it.kv_start * pg.max_pages + (kt * kBN) / pg.page_size];
+        return block_table[(int64_t)it.kv_start * pg.max_pages + (it.kv_lo + kt * kBN) / pg.page_size];
     };
     // tile kt into `stage` (`entry`: its table entry, paged cache only)
     auto issue_tile = [&](int kt, int stage, int entry) __attribute__((always_inline)) {
         uint8_t* dst = smem + stage * kTileBytes + wave * kGroups * 1024;
-        const int key0 = kt * kBN;
+        const int key0 = it.kv_lo + kt * kBN;
         uint64_t row0 = (uint64_t)key0;
         if constexpr (kPaged) {
             const int page = entry < 0 ? 0 : (entry >= pg.num_pages ? pg.num_pages - 1 : entry);
@@ -259,7 +261,7 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
         }
         sacc = acc;
         if constexpr (kMasked) {
-            const int key0 = kt * kBN;
+            const int key0 = it.kv_lo + kt * kBN;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = key0 + (i >> 2) * 8 + g * 4 + (i & 3);
@@ -340,9 +342,16 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     // tile j, then the softmax of tile j (against the new running maximum)
     // interleaved with PV of tile j-1 (whose P was taken against the old
     // one), and last, if the maximum moved, O *= 2^(m_old - m_new).
-    const int n_tiles = (it.kv_hi + kBN - 1) / kBN;
-    const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
-    const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
+    // the item's keys [kv_lo, kv_hi) as tiles 0 .. n_tiles-1 (kv_lo is a
+    // multiple of 32); n_full: tiles every row of the wave sees whole,
+    // n_wave: tiles with a key some row of the wave sees
+    const int n_tiles = (it.kv_hi - it.kv_lo + kBN - 1) / kBN;
+    int nf = wave_lo > it.kv_lo ? (wave_lo - it.kv_lo) / kBN : 0;
+    int nw = wave_hi > it.kv_lo ? (wave_hi - it.kv_lo + kBN - 1) / kBN : 0;
+    nf = nf < n_tiles ? nf : n_tiles;
+    nw = nw < n_tiles ? nw : n_tiles;
+    const int n_full = __builtin_amdgcn_readfirstlane(nf);
+    const int n_wave = __builtin_amdgcn_readfirstlane(nw);
     // tiles are issued in order; with a paged cache the next tile's table
     // entry is read one issue ahead
     int iss_page = 0;
@@ -414,6 +423,25 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     if (my_row >= it.n_rows) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
     const int64_t rho = (int64_t)it.row0 + my_row;
+    if (it.part >= 0) {
+        // a KV split: fp32 partial state over this item's keys
+        float* pdst = part_o + ((int64_t)it.part * part_rows + rho) * kDv;
+#pragma unroll
+        for (int db = 0; db < kDvBlocks; ++db) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int dv = db * 32 + grp * 8 + g * 4;
+                f32x4_t o4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = oacc[db][grp * 4 + e] * inv;
+                *reinterpret_cast<f32x4_t*>(pdst + dv) = o4;
+            }
+        }
+        if (g == 0)
+            part_lse[(int64_t)it.part * part_rows + rho] =
+                ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
+        return;
+    }
     uint16_t* dst = out + rho * kDv;
 #pragma unroll
     for (int db = 0; db < kDvBlocks; ++db) {
@@ -435,7 +463,8 @@ int prefill_absorbed_block_m() { return kBM; }
 
 hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, const void* q,
                                    const void* kv, void* out, float* lse, int num_heads,
-                                   float sm_scale, hipStream_t stream, const PagedKv* paged) {
+                                   float sm_scale, hipStream_t stream, const PagedKv* paged,
+                                   float* part_o, float* part_lse, int64_t part_rows) {
     if (n_items <= 0) return hipSuccess;
     if (n_items > 0x7fffffff) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
@@ -444,12 +473,63 @@ hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, con
         hipLaunchKernelGGL(prefill_absorbed_kernel<true>, dim3((unsigned)n_items), dim3(kThreads), 0,
                            stream, items, static_cast<const uint16_t*>(q),
                            static_cast<const uint16_t*>(kv), static_cast<uint16_t*>(out), lse,
-                           num_heads, scale_log2, pg, pg.block_table);
+                           num_heads, scale_log2, pg, pg.block_table, part_o, part_lse, part_rows);
     else
         hipLaunchKernelGGL(prefill_absorbed_kernel<false>, dim3((unsigned)n_items), dim3(kThreads), 0,
                            stream, items, static_cast<const uint16_t*>(q),
                            static_cast<const uint16_t*>(kv), static_cast<uint16_t*>(out), lse,
-                           num_heads, scale_log2, pg, nullptr);
+                           num_heads, scale_log2, pg, nullptr, part_o, part_lse, part_rows);
+    return hipGetLastError();
+}
+
+namespace {
+
+// Combine the KV splits of each row (the flash-decoding split of one row's
+// keys, merged with the same log-sum-exp weights as merge_state):
+//   lse = ln sum_s e^lse_s,  o = sum_s e^(lse_s - lse) o_s;
+// splits with lse = -inf carry weight 0; all -inf gives o = 0, lse = -inf.
+// One row per 128 lanes, 4 dims per lane (16-byte loads of each partial).
+constexpr int kMergeThreads = 256;
+constexpr int kMaxSplits = 64;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
+    int64_t rows, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+    if (row >= rows) return;
+    const int c = threadIdx.x & 127;
+    float mx = -INFINITY;
+    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[(int64_t)s * rows + row]);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float sum = 0.f;
+    if (mx != -INFINITY) {
+        for (int s = 0; s < splits; ++s) {
+            const float ls = part_lse[(int64_t)s * rows + row];
+            if (ls == -INFINITY) continue;
+            const float w = __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part_o + ((int64_t)s * rows + row) * kDv + c * 4);
+            acc += w * v;
+            sum += w;
+        }
+    }
+    const float inv = sum > 0.f ? 1.0f / sum : 0.0f;
+    bf16x4_t o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x4_t*>(out + row * kDv + c * 4) = o4;
+    if (c == 0 && lse != nullptr) lse[row] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_merge_splits(const float* part_o, const float* part_lse, int splits,
+                               int64_t rows, void* out, float* lse, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+    const int64_t blocks = (rows + 1) / 2;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream,
+                       part_o, part_lse, splits, rows, static_cast<uint16_t*>(out), lse);
     return hipGetLastError();
 }
 

@@ -312,13 +312,19 @@ def _check_latent_plan(qo_lens, kv_lens, heads, causal):
     kv = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
     items = mra.absorbed_plan_items(qo, kv, heads, causal)
     assert len(items) % 8 == 0
+    real = items[items[:, 1] > 0]
+    assert not np.any(items[items[:, 1] == 0]), "padding items are all zero"
+    parts = set(int(p) for p in real[:, 8])
+    splits = 1 if parts <= {-1} else len(parts)
+    assert parts == ({-1} if splits == 1 else set(range(splits)))
     cover = np.zeros(int(qo[-1]) * heads, dtype=np.int64)
+    ranges = {}
     groups = {}
-    for i, (row0, n_rows, seq_row0, kv_hi, kv_start, kv_len, diag_base, res) in enumerate(items):
+    for i, (row0, n_rows, seq_row0, kv_hi, kv_start, kv_len, diag_base, kv_lo, part,
+            p0, p1, p2) in enumerate(items):
         if n_rows == 0:
-            assert not np.any(items[i]), "padding items are all zero"
             continue
-        assert 0 < n_rows <= ABS_BM and res == 0
+        assert 0 < n_rows <= ABS_BM and p0 == p1 == p2 == 0
         seq = int(np.searchsorted(qo * heads, row0, side="right")) - 1
         assert seq_row0 == qo[seq] * heads
         assert (row0 - seq_row0) % ABS_BM == 0
@@ -326,12 +332,25 @@ def _check_latent_plan(qo_lens, kv_lens, heads, causal):
         assert kv_start == kv[seq] and kv_len == kv[seq + 1] - kv[seq]
         qo_len = qo[seq + 1] - qo[seq]
         assert diag_base == (kv_len - qo_len if causal else kv_len)
-        last_tok = (row0 + n_rows - 1 - seq_row0) // heads
-        assert kv_hi == min(kv_len, max(0, diag_base + last_tok + 1))
+        assert kv_lo % 32 == 0 and 0 <= kv_lo <= kv_hi
         cover[row0:row0 + n_rows] += 1
+        ranges.setdefault(row0, []).append((int(part), int(kv_lo), int(kv_hi)))
         groups.setdefault(seq, set()).add(i % 8)
-    assert np.all(cover == 1)
-    return items, groups
+    assert np.all(cover == splits)
+    # the splits of a tile cover the keys its last row sees, in order, once
+    for row0, rs in ranges.items():
+        seq = int(np.searchsorted(qo * heads, row0, side="right")) - 1
+        n_rows = next(int(it[1]) for it in real if it[0] == row0)
+        qo_len, kv_len = qo[seq + 1] - qo[seq], kv[seq + 1] - kv[seq]
+        diag = kv_len - qo_len if causal else kv_len
+        last_tok = (row0 + n_rows - 1 - qo[seq] * heads) // heads
+        want_hi = min(kv_len, max(0, diag + last_tok + 1))
+        rs.sort()
+        assert [r[0] for r in rs] == ([-1] if splits == 1 else list(range(splits)))
+        assert rs[0][1] == 0 and rs[-1][2] == want_hi
+        for (pa, lo_a, hi_a), (pb, lo_b, hi_b) in zip(rs, rs[1:]):
+            assert hi_a == lo_b or (hi_a == want_hi and lo_b >= want_hi - 31)
+    return items, groups, splits
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -343,9 +362,23 @@ def test_absorbed_partition_covers_every_row_once(causal):
 
 def test_absorbed_partition_keeps_short_sequences_on_one_xcd():
     # at most 256 tiles per group: a sequence with fewer tiles stays on one XCD
-    items, groups = _check_latent_plan([100, 40, 4000, 8], [100, 40, 4000, 8], 16, True)
+    items, groups, splits = _check_latent_plan([100, 40, 4000, 8], [100, 40, 4000, 8], 16, True)
+    assert splits == 1
     assert len(groups[0]) == 1 and len(groups[1]) == 1 and len(groups[3]) == 1
     assert len(groups[2]) == 2         # 4000 x 16 rows = 500 tiles: two groups
+
+
+def test_absorbed_partition_splits_keys_when_tiles_are_few():
+    # a decode step (one token per sequence) over long prefixes: the keys of
+    # each tile are shared out over several items
+    _, _, splits = _check_latent_plan([1] * 16, [4096] * 16, 128, True)
+    assert splits == 8
+    _, _, splits = _check_latent_plan([1] * 4, [200, 37, 300, 1], 128, True)
+    assert 1 < splits <= 2           # at least four 32-key tiles per split
+    _, _, splits = _check_latent_plan([1] * 4, [64, 37, 100, 1], 128, False)
+    assert splits == 1               # too few keys to split
+    _, _, splits = _check_latent_plan([2048] * 2, [2048] * 2, 128, True)
+    assert splits == 1               # enough row tiles
 
 
 def test_absorbed_prefill_rejects_invalid_arguments_before_any_hip_call():

@@ -596,3 +596,41 @@ def test_absorbed_paged_prefix_against_the_oracle():
     torch.cuda.synchronize()
     ro, rl = oracle.absorbed(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
     check(o, l, ro, rl, torch.bfloat16, "absorbed paged prefix")
+
+
+def test_absorbed_kv_splits_against_the_oracle():
+    # few row tiles over long key ranges: the library splits each tile's keys
+    # over several items and merges their partial states; rows of one tile
+    # see different key counts (causal, 3 tokens x 16 heads in one tile)
+    qo, kv = [3, 1, 2], [3000, 777, 64]
+    x = workloads.absorbed_inputs(qo, kv, 16, seed=49, causal=True)
+    items = mra.absorbed_plan_items(x.qo_indptr, x.kv_indptr, 16, True)
+    assert items[:, 8].max() > 0, "expected a KV split"
+    _absorbed_parity(x, "KV splits, causal")
+    x = workloads.absorbed_inputs(qo, kv, 16, seed=50, causal=False)
+    _absorbed_parity(x, "KV splits, non-causal")
+
+
+def test_absorbed_decode_batch_sampled():
+    # a decode step of 16 requests over 4096-token prefixes (8 KV splits)
+    x = workloads.absorbed_inputs([1] * 16, [4096] * 16, 128, seed=51, causal=True)
+    _flush("[gpu] absorbed decode batch 16 x 4096")
+    o, lse = mra.absorbed_prefill(x.q.to(DEV), x.kv.to(DEV), x.qo_indptr, x.kv_indptr, True,
+                                  x.sm_scale)
+    torch.cuda.synchronize()
+    _row_properties(o, lse)
+    rows = [0, 5, 11, 15]
+    ro, rl = oracle.absorbed(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale, rows=rows)
+    idx = torch.tensor(rows)
+    check(o[idx].cpu(), lse[idx].cpu(), ro, rl, torch.bfloat16, "absorbed decode batch")
+
+
+def test_absorbed_paged_decode_matches_contiguous():
+    x = workloads.absorbed_inputs([1, 1, 2], [1500, 300, 2000], 64, seed=52, causal=True)
+    pool, table = _latent_paged_cache(x, 64, extra_pages=4, seed=12)
+    q, kv = x.q.to(DEV), x.kv.to(DEV)
+    ref_o, ref_l = mra.absorbed_prefill(q, kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    o, l = mra.absorbed_prefill_paged(q, pool.to(DEV), x.qo_indptr, x.kv_indptr, table.to(DEV),
+                                      True, x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
