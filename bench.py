@@ -87,6 +87,15 @@ def profile_traffic(profile, source):
         return None
 
 
+def device_info(torch):
+    """What the peaks are set against: the device's name and CU count as the
+    runtime reports them; the peaks themselves are MI355X's published ones."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "peak_basis": "bf16 dense 256 CU x 4096 flop/clk x 2.4 GHz; HBM3E 8 TB/s"}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,9 +118,13 @@ def time_prefill(mra, torch, x, steps, warmup, n_xcd):
     out = torch.empty((x.q.shape[0], x.num_heads, 128), dtype=x.q.dtype, device=x.q.device)
     lse = torch.empty((x.q.shape[0], x.num_heads), dtype=torch.float32, device=x.q.device)
 
+    plan_s = []
+
     def step(ev=None):
+        t = time.perf_counter()
         plan.plan(x.qo_indptr, x.kv_indptr, x.num_heads, x.causal, x.q.dtype)
         plan.upload()
+        plan_s.append(time.perf_counter() - t)
         if ev is not None:
             ev[0].record()
         plan.run(x.q, x.k, x.v, x.sm_scale, out=out, lse=lse)
@@ -121,6 +134,7 @@ def time_prefill(mra, torch, x, steps, warmup, n_xcd):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    plan_s.clear()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     t0 = time.perf_counter()
@@ -130,6 +144,7 @@ def time_prefill(mra, torch, x, steps, warmup, n_xcd):
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     info = plan.info()
+    info["plan_ms"] = sum(plan_s) / len(plan_s) * 1e3
     return wall, kern_ms, info
 
 
@@ -160,7 +175,16 @@ def cpu_baseline(oracle, torch, x, target_s, seed=0):
     n2 = max(64, min(200000, int(64 * target_s / max(dt, 1e-3))))
     dt, pairs, n = run(n2)
     flops = 2.0 * pairs * 320
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model,
             "kind": "oracle",
             "sample": f"{n} random query rows x {len(heads)} heads (heads {heads}) of the same "
                       f"batch, {pairs} visible pairs, {dt:.1f} s, fp64"}
@@ -186,8 +210,23 @@ def time_merge(mra, torch, workloads, steps, warmup):
     rows = tokens * heads
     bytes_ = rows * (3 * 128 * 2 + 3 * 4)      # read o_a, o_b, lse_a, lse_b; write o, lse
     gbs = bytes_ / (ms * 1e-3) / 1e9
+    # a plain device-to-device copy of the same byte count, as a measured ceiling
+    src = torch.empty(bytes_ // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() / (c0.elapsed_time(c1) / steps * 1e-3) / 1e9
+    del src, dst
     return {"workload": f"merge_state {tokens} tokens x {heads} heads, bf16",
             "kernel_ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "device_copy_GB/s": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": profile_traffic("merge_state_16384x128_bf16.txt",
@@ -208,26 +247,42 @@ def time_chunked(mra, torch, workloads, steps, warmup):
             for _ in passes]
     fo, fl = torch.empty_like(outs[0][0]), torch.empty_like(outs[0][1])
 
-    def step():
-        for (p, x), (o, l) in zip(passes, outs):
+    # HIP events between the stages: 3 passes, then 2 merges
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for i, ((p, x), (o, l)) in enumerate(zip(passes, outs)):
             p.run(x.q, x.k, x.v, x.sm_scale, out=o, lse=l)
+            if ev is not None:
+                ev[1 + i].record()
         mra.merge_state(outs[0][0], outs[0][1], outs[1][0], outs[1][1], out=fo, out_lse=fl)
+        if ev is not None:
+            ev[4].record()
         mra.merge_state(fo, fl, outs[2][0], outs[2][1], out=fo, out_lse=fl)
+        if ev is not None:
+            ev[5].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(evs[i])
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
+    stage = [sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps for k in range(5)]
     pairs = sum(visible_pairs(x.qo_indptr, x.kv_indptr, x.causal) for x in c.chunks + [m])
     flops = 2.0 * m.num_heads * pairs * 320
     return {"workload": "chunked_prefill: 8 x (2048 new causal + 2 x 4096 context), 128 heads, "
                         "3 prefill passes + 2 merge_state",
             "ms_per_step": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
-            "flops_per_step": flops}
+            "flops_per_step": flops,
+            "context_pass_ms": [round(stage[0], 4), round(stage[1], 4)],
+            "new_token_pass_ms": round(stage[2], 4),
+            "passes_ms": round(stage[0] + stage[1] + stage[2], 4),
+            "merges_ms": round(stage[3] + stage[4], 4)}
 
 
 def time_paged_context(mra, torch, workloads, steps, warmup, page=64):
@@ -547,7 +602,10 @@ def main():
                      "traffic": profile_traffic("prefill_bf16_deepseek_v3_batch.txt",
                                                 "mla_ragged_chunked_amd/csrc/prefill_bf16.hip"),
                      "kernel": "prefill_bf16_kernel",
-                     "kernel_ms": round(k_ms, 4)},
+                     "kernel_ms": round(k_ms, 4),
+                     "kernel_ms_median": round(sorted(kern_ms)[len(kern_ms) // 2], 4),
+                     "host_plan_ms": round(info["plan_ms"], 4)},
+        "device": device_info(torch),
     }
     if args.cpu_seconds > 0:
         import oracle
