@@ -504,29 +504,36 @@ def time_absorbed_decode(mra, torch, workloads, steps, warmup, batch=64, prefix=
     pairs = visible_pairs(x.qo_indptr, x.kv_indptr, x.causal)
     flops = 2.0 * H * pairs * (576 + 512)
     nbytes = 2.0 * (batch * H * 576 + batch * prefix * 576 + batch * H * 512) + 4.0 * batch * H
-    items = mra.absorbed_plan_items(x.qo_indptr, x.kv_indptr, H, True)
-    splits = int(items[:, 8].max()) + 1 if len(items) else 1
-    out, lse = mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
-    for _ in range(warmup):
-        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale, out=out,
-                             lse=lse)
-    torch.cuda.synchronize()
+    # planned once, run per layer (the plan/run split); the one-shot call,
+    # which plans on the host every time, is timed next to it
+    plan = mra.AbsorbedPlan().plan(x.qo_indptr, x.kv_indptr, H, True).upload()
+    splits = plan.info()["kv_splits"]
+    out, lse = plan.run(x.q, x.kv, x.sm_scale)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale, out=out,
-                             lse=lse)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: plan.run(x.q, x.kv, x.sm_scale, out=out, lse=lse))
+    ms_one_shot = timed(lambda: mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True,
+                                                     x.sm_scale, out=out, lse=lse))
     gbs = nbytes / ms / 1e6
     return {"workload": f"absorbed decode: {batch} requests x 1 token over {prefix}-token latent "
                         f"caches, {H} heads, bf16",
-            "step_ms": round(ms, 4), "kv_splits": splits,
+            "step_ms": round(ms, 4), "one_shot_ms": round(ms_one_shot, 4), "kv_splits": splits,
             "TFLOP/s": round(flops / ms / 1e9, 1), "GB/s": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "note": "step = absorbed kernel + KV-split merge, both kernels"}}
+                         "note": "step = one run of a plan made once: the absorbed kernel "
+                                 "and the KV-split merge"}}
 
 
 def main():

@@ -330,6 +330,39 @@ int mla_absorbed_prefill_paged(const void *q, const void *kv_cache, const int32_
                                void *out, float *lse, void *stream);
 
 /*
+ * Plan-once / run-per-layer form of the absorbed prefill (the plan()/run()
+ * split of "vllm.v1.attention.backends.mla.prefill.flashinfer": the work list
+ * depends only on the indptrs, so one plan serves every layer of a step).
+ *   create / destroy  the plan object (destroy synchronises its device).
+ *   build    plans from HOST indptrs as mla_absorbed_prefill does (including
+ *            the choice of KV splits); paged = 1 plans for run_paged.
+ *   upload   copies the work list to the current device on `stream` and
+ *            allocates the split buffer (a second upload after a rebuild may
+ *            reallocate it, after synchronising the device).
+ *   run      one kernel (plus the split merge) on `stream`: q, kv, out, lse
+ *            as for mla_absorbed_prefill; run_paged as for
+ *            mla_absorbed_prefill_paged.
+ *   info     number of work items and KV splits.
+ * Runs of one plan that uses KV splits share its split buffer: they must not
+ * overlap (issue them on one stream, or order them). Errors: MLA_ESTATE when
+ * the plan is not built/uploaded, or built for the other cache kind.
+ */
+typedef struct mla_absorbed_plan mla_absorbed_plan;
+int mla_absorbed_plan_create(mla_absorbed_plan **out);
+void mla_absorbed_plan_destroy(mla_absorbed_plan *plan);
+int mla_absorbed_plan_build(mla_absorbed_plan *plan, const int32_t *qo_indptr,
+                            const int32_t *kv_indptr, int32_t batch, int32_t num_heads,
+                            int32_t causal, int32_t paged);
+int mla_absorbed_plan_upload(mla_absorbed_plan *plan, void *stream);
+int mla_absorbed_run(const mla_absorbed_plan *plan, const void *q, const void *kv, float sm_scale,
+                     void *out, float *lse, void *stream);
+int mla_absorbed_run_paged(const mla_absorbed_plan *plan, const void *q, const void *kv_cache,
+                           const int32_t *block_table, int32_t max_pages, int32_t page_size,
+                           int32_t num_pages, float sm_scale, void *out, float *lse,
+                           void *stream);
+int mla_absorbed_plan_info(const mla_absorbed_plan *plan, int64_t *n_items, int32_t *splits);
+
+/*
  * Host-only view of the absorbed prefill's work list (no HIP call): writes
  * *n_items and, if dst is non-NULL and capacity_items suffices, the items
  * as 12 int32 each: {row0, n_rows, seq_row0, kv_hi, kv_start, kv_len,

@@ -23,7 +23,7 @@ import numpy as np
 import torch
 
 __all__ = ["ragged_prefill", "ragged_prefill_paged", "merge_state", "decompress_kv",
-           "absorbed_prefill", "absorbed_prefill_paged", "absorbed_plan_items", "Plan", "DevicePlan", "MlaError", "lib",
+           "absorbed_prefill", "absorbed_prefill_paged", "absorbed_plan_items", "AbsorbedPlan", "Plan", "DevicePlan", "MlaError", "lib",
            "LIB_PATH", "DQK", "DVO", "DLAT", "DROPE", "EXPORTED_SYMBOLS"]
 
 DQK, DVO, DLAT, DROPE = 192, 128, 512, 64
@@ -39,7 +39,9 @@ EXPORTED_SYMBOLS = [
     "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
     "mla_ragged_prefill_device_plan", "mla_ragged_prefill_paged",
     "mla_merge_state", "mla_decompress_kv", "mla_absorbed_prefill", "mla_absorbed_plan_items",
-    "mla_absorbed_prefill_paged",
+    "mla_absorbed_prefill_paged", "mla_absorbed_plan_create", "mla_absorbed_plan_destroy",
+    "mla_absorbed_plan_build", "mla_absorbed_plan_upload", "mla_absorbed_run",
+    "mla_absorbed_run_paged", "mla_absorbed_plan_info",
 ]
 
 
@@ -93,6 +95,13 @@ def lib():
                                     ctypes.c_int),
         "mla_absorbed_prefill_paged": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, P, P, P],
                                        ctypes.c_int),
+        "mla_absorbed_plan_create": ([ctypes.POINTER(P)], ctypes.c_int),
+        "mla_absorbed_plan_destroy": ([P], None),
+        "mla_absorbed_plan_build": ([P, P, P, I32, I32, I32, I32], ctypes.c_int),
+        "mla_absorbed_plan_upload": ([P, P], ctypes.c_int),
+        "mla_absorbed_run": ([P, P, P, F, P, P, P], ctypes.c_int),
+        "mla_absorbed_run_paged": ([P, P, P, P, I32, I32, I32, F, P, P, P], ctypes.c_int),
+        "mla_absorbed_plan_info": ([P, ctypes.POINTER(I64), ctypes.POINTER(I32)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(l, name)
@@ -500,3 +509,100 @@ def absorbed_prefill_paged(q: torch.Tensor, kv_cache: torch.Tensor, qo_indptr, k
             _stream(q.device)),
             "mla_absorbed_prefill_paged")
     return (out, lse) if return_lse else out
+
+
+class AbsorbedPlan:
+    """Work list of the absorbed prefill for one ragged batch: plan once
+    (host indptrs), upload, then run per layer (contiguous or paged cache)."""
+
+    def __init__(self):
+        self._lib = lib()
+        h = ctypes.c_void_p()
+        _check(self._lib.mla_absorbed_plan_create(ctypes.byref(h)), "mla_absorbed_plan_create")
+        self._h = h
+        self.num_heads = 0
+        self.tq = 0
+        self.batch = 0
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.mla_absorbed_plan_destroy(h)
+            self._h = None
+
+    def plan(self, qo_indptr, kv_indptr, num_heads: int, causal: bool,
+             paged: bool = False) -> "AbsorbedPlan":
+        qo, kv = _indptr(qo_indptr), _indptr(kv_indptr)
+        if len(qo) != len(kv) or len(qo) < 1:
+            raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+        _check(self._lib.mla_absorbed_plan_build(self._h, qo.ctypes.data, kv.ctypes.data,
+                                                 len(qo) - 1, int(num_heads), int(bool(causal)),
+                                                 int(bool(paged))),
+               "mla_absorbed_plan_build")
+        self.num_heads, self.tq, self.batch = int(num_heads), int(qo[-1]), len(qo) - 1
+        return self
+
+    def upload(self, device=None) -> "AbsorbedPlan":
+        dev = torch.device("cuda" if device is None else device)
+        with torch.cuda.device(dev):
+            _check(self._lib.mla_absorbed_plan_upload(self._h, _stream(dev)),
+                   "mla_absorbed_plan_upload")
+        return self
+
+    def info(self):
+        n = ctypes.c_int64(0)
+        sp = ctypes.c_int32(0)
+        _check(self._lib.mla_absorbed_plan_info(self._h, ctypes.byref(n), ctypes.byref(sp)),
+               "mla_absorbed_plan_info")
+        return {"n_items": n.value, "kv_splits": sp.value}
+
+    def _outputs(self, q, out, lse, return_lse):
+        _dev_tensor(q, "q")
+        if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != DLAT + DROPE:
+            raise ValueError("q must be bf16 [Tq,H,576]")
+        if q.shape[0] != self.tq or q.shape[1] != self.num_heads:
+            raise ValueError("q does not match the planned tokens / heads")
+        if out is None:
+            out = torch.empty((self.tq, self.num_heads, DLAT), dtype=torch.bfloat16,
+                              device=q.device)
+        if return_lse and lse is None:
+            lse = torch.empty((self.tq, self.num_heads), dtype=torch.float32, device=q.device)
+        _dev_tensor(out, "out")
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (self.tq, self.num_heads, DLAT):
+            raise ValueError("out must be bf16 [Tq,H,512]")
+        if return_lse:
+            _dev_tensor(lse, "lse")
+            if lse.dtype != torch.float32 or tuple(lse.shape) != (self.tq, self.num_heads):
+                raise ValueError("lse must be fp32 [Tq,H]")
+        return out, lse
+
+    def run(self, q, kv, sm_scale: float, out=None, lse=None, return_lse: bool = True):
+        _dev_tensor(kv, "kv")
+        if kv.dtype != torch.bfloat16 or kv.dim() != 2 or kv.shape[1] != DLAT + DROPE:
+            raise ValueError("kv must be bf16 [Tk,576]")
+        out, lse = self._outputs(q, out, lse, return_lse)
+        with torch.cuda.device(q.device):
+            _check(self._lib.mla_absorbed_run(self._h, _ptr(q), _ptr(kv), float(sm_scale),
+                                              _ptr(out), _ptr(lse) if return_lse else None,
+                                              _stream(q.device)),
+                   "mla_absorbed_run")
+        return (out, lse) if return_lse else out
+
+    def run_paged(self, q, kv_cache, block_table, sm_scale: float, out=None, lse=None,
+                  return_lse: bool = True):
+        _dev_tensor(kv_cache, "kv_cache")
+        _dev_tensor(block_table, "block_table")
+        if kv_cache.dtype != torch.bfloat16 or kv_cache.dim() != 3 or \
+                kv_cache.shape[2] != DLAT + DROPE:
+            raise ValueError("kv_cache must be bf16 [num_pages,page_size,576]")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+                block_table.shape[0] != self.batch:
+            raise ValueError("block_table must be int32 [batch, max_pages]")
+        out, lse = self._outputs(q, out, lse, return_lse)
+        with torch.cuda.device(q.device):
+            _check(self._lib.mla_absorbed_run_paged(
+                self._h, _ptr(q), _ptr(kv_cache), _ptr(block_table), block_table.shape[1],
+                kv_cache.shape[1], kv_cache.shape[0], float(sm_scale), _ptr(out),
+                _ptr(lse) if return_lse else None, _stream(q.device)),
+                "mla_absorbed_run_paged")
+        return (out, lse) if return_lse else out

@@ -140,6 +140,30 @@ struct mla_plan {
     DeviceWorkList<WorkItem> dwl;
 };
 
+struct mla_absorbed_plan {
+    std::vector<mla::LatentItem> items;
+    int64_t tq = 0, tk = 0, rows = 0;
+    int32_t batch = 0, num_heads = 0, causal = 0, splits = 1, max_kv_len = 0;
+    bool paged = false;           // items carry the sequence index in kv_start
+    bool planned = false;
+    bool uploaded = false;
+    DeviceWorkList<mla::LatentItem> dwl;
+    // fp32 partial states of the KV splits (grow-only)
+    void* part = nullptr;
+    size_t part_bytes = 0;
+    int part_device = -1;
+    ~mla_absorbed_plan() {
+        if (part != nullptr) {
+            int keep = -1;
+            (void)hipGetDevice(&keep);
+            (void)hipSetDevice(part_device);
+            (void)hipDeviceSynchronize();
+            (void)hipFree(part);
+            (void)hipSetDevice(keep);
+        }
+    }
+};
+
 namespace {
 
 int check_dtype(int32_t dtype) {
@@ -291,17 +315,9 @@ int oneshot(const void* q, const void* k, const void* v, const int32_t* qo_indpt
     return do_run(p, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream), paged);
 }
 
-// Weight-absorbed prefill: host-planned work list kept per (device, stream).
-struct AbsorbedState {
-    std::vector<mla::LatentItem> items;
-    DeviceWorkList<mla::LatentItem> dwl;
-    // fp32 partial states of KV splits (grow-only; only this stream uses it)
-    void* part = nullptr;
-    size_t part_bytes = 0;
-    int part_device = -1;
-};
+// Weight-absorbed prefill: one-shot calls keep one plan per (device, stream).
 std::mutex g_absorbed_mu;
-std::map<std::pair<int, void*>, AbsorbedState*>* g_absorbed = nullptr;
+std::map<std::pair<int, void*>, mla_absorbed_plan*>* g_absorbed = nullptr;
 
 int absorbed_plan(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_heads,
                   int32_t causal, std::vector<mla::LatentItem>& items, bool paged = false,
@@ -333,84 +349,160 @@ int absorbed_plan(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t n
     return MLA_OK;
 }
 
-// One absorbed prefill call (contiguous cache, or a page pool when `pg`).
+int absorbed_build(mla_absorbed_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch,
+                   int32_t num_heads, int32_t causal, bool paged) {
+    if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    p->planned = false;
+    p->uploaded = false;
+    int splits = 1;
+    std::vector<mla::LatentItem> items;
+    if (int s = absorbed_plan(qo, kv, batch, num_heads, causal, items, paged, &splits)) return s;
+    p->items.swap(items);
+    p->tq = batch > 0 ? qo[batch] : 0;
+    p->tk = batch > 0 ? kv[batch] : 0;
+    p->rows = p->tq * num_heads;
+    p->batch = batch;
+    p->num_heads = num_heads;
+    p->causal = causal;
+    p->splits = splits;
+    p->max_kv_len = 0;
+    for (int32_t b = 0; b < batch; ++b)
+        p->max_kv_len = std::max<int32_t>(p->max_kv_len, kv[b + 1] - kv[b]);
+    p->paged = paged;
+    p->planned = true;
+    return MLA_OK;
+}
+
+int absorbed_upload(mla_absorbed_plan* p, hipStream_t stream) {
+    if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (!p->planned) return fail(MLA_ESTATE, "plan has not been built");
+    p->uploaded = false;
+    if (p->items.empty()) {
+        p->uploaded = true;
+        return MLA_OK;
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (p->splits > 1) {
+        const size_t need = static_cast<size_t>(p->splits) * static_cast<size_t>(p->rows) *
+                            (MLA_LATENT_DIM + 1) * sizeof(float);
+        if (p->part != nullptr && (p->part_bytes < need || p->part_device != dev)) {
+            // earlier runs of this plan may still be using it
+            int keep = dev;
+            (void)hipSetDevice(p->part_device);
+            e = hipDeviceSynchronize();
+            (void)hipFree(p->part);
+            (void)hipSetDevice(keep);
+            p->part = nullptr;
+            p->part_bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        }
+        if (p->part == nullptr) {
+            e = hipMalloc(&p->part, need);
+            if (e != hipSuccess) {
+                p->part = nullptr;
+                return fail(MLA_ENOMEM, "hipMalloc of the KV-split partial states failed");
+            }
+            p->part_bytes = need;
+            p->part_device = dev;
+        }
+    }
+    if (int r = p->dwl.upload(p->items, stream)) return r;
+    p->uploaded = true;
+    return MLA_OK;
+}
+
+// One run of an uploaded plan (contiguous cache, or a page pool when `pg`).
+int absorbed_run(const mla_absorbed_plan* p, const void* q, const void* kv, float sm_scale,
+                 void* out, float* lse, hipStream_t stream, const mla::PagedKv* pg) {
+    if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (!p->planned) return fail(MLA_ESTATE, "plan has not been built");
+    if (!p->uploaded) return fail(MLA_ESTATE, "plan has not been uploaded");
+    if (p->paged != (pg != nullptr)) return fail(MLA_ESTATE, "plan and call disagree on paged cache");
+    if (int s = check_scale(sm_scale)) return s;
+    if (p->tq > 0 && (q == nullptr || out == nullptr))
+        return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
+    if ((p->tk > 0 || pg != nullptr) && kv == nullptr)
+        return fail(MLA_EINVAL, "kv must be non-NULL when there are keys");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
+        return fail(MLA_EINVAL, "q, kv, out and lse must be 16-byte aligned");
+    if (pg != nullptr && p->max_kv_len > static_cast<int64_t>(pg->max_pages) * pg->page_size)
+        return fail(MLA_EINVAL, "a sequence's context exceeds max_pages x page_size");
+    if (p->items.empty()) return MLA_OK;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != p->dwl.device || (p->splits > 1 && dev != p->part_device))
+        return fail(MLA_ESTATE, "plan was uploaded on another device");
+    float* part_o = nullptr;
+    float* part_lse = nullptr;
+    if (p->splits > 1) {
+        part_o = static_cast<float*>(p->part);
+        part_lse = part_o + static_cast<size_t>(p->splits) * p->rows * MLA_LATENT_DIM;
+    }
+    e = mla::launch_prefill_absorbed(p->dwl.dev, static_cast<int64_t>(p->items.size()), q, kv,
+                                     out, lse, p->num_heads, sm_scale, stream, pg, part_o,
+                                     part_lse, p->rows);
+    if (e != hipSuccess) return hip_fail(e, "absorbed prefill kernel launch");
+    if (p->splits > 1) {
+        e = mla::launch_merge_splits(part_o, part_lse, p->splits, p->rows, out, lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "KV-split merge kernel launch");
+    }
+    return MLA_OK;
+}
+
+// One-shot absorbed call (plan + upload + run) with a plan kept per (device,
+// stream); contiguous cache, or a page pool when `pg`.
 int absorbed_call(const void* q, const void* kv, const int32_t* qo_indptr,
                   const int32_t* kv_indptr, int32_t batch, int32_t num_heads, int32_t causal,
                   float sm_scale, void* out, float* lse, void* stream, const mla::PagedKv* pg) {
     if (int s = check_scale(sm_scale)) return s;
-    std::vector<mla::LatentItem> items;
-    int splits = 1;
-    if (int s = absorbed_plan(qo_indptr, kv_indptr, batch, num_heads, causal, items, pg != nullptr,
-                              &splits))
+    mla_absorbed_plan check;
+    if (int s = absorbed_build(&check, qo_indptr, kv_indptr, batch, num_heads, causal, pg != nullptr))
         return s;
-    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
-    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
-    if (tq > 0 && (q == nullptr || out == nullptr))
+    if (check.tq > 0 && (q == nullptr || out == nullptr))
         return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
-    if ((tk > 0 || pg != nullptr) && kv == nullptr)
+    if ((check.tk > 0 || pg != nullptr) && kv == nullptr)
         return fail(MLA_EINVAL, "kv must be non-NULL when there are keys");
     if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
         return fail(MLA_EINVAL, "q, kv, out and lse must be 16-byte aligned");
-    if (items.empty()) return MLA_OK;
+    if (check.items.empty()) return MLA_OK;
 
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    AbsorbedState* st = nullptr;
+    mla_absorbed_plan* p = nullptr;
     {
         std::lock_guard<std::mutex> lock(g_absorbed_mu);
         if (g_absorbed == nullptr)
-            g_absorbed = new (std::nothrow) std::map<std::pair<int, void*>, AbsorbedState*>();
+            g_absorbed = new (std::nothrow) std::map<std::pair<int, void*>, mla_absorbed_plan*>();
         if (g_absorbed == nullptr) return fail(MLA_ENOMEM, "absorbed plan table");
         auto key = std::make_pair(dev, stream);
         auto it = g_absorbed->find(key);
         if (it == g_absorbed->end()) {
-            st = new (std::nothrow) AbsorbedState();
-            if (st == nullptr) return fail(MLA_ENOMEM, "absorbed plan");
-            (*g_absorbed)[key] = st;
+            p = new (std::nothrow) mla_absorbed_plan();
+            if (p == nullptr) return fail(MLA_ENOMEM, "absorbed plan");
+            (*g_absorbed)[key] = p;
         } else {
-            st = it->second;
+            p = it->second;
         }
     }
-    st->items.swap(items);
+    // the work list moves into the per-stream plan; its device buffers stay
+    p->items.swap(check.items);
+    p->tq = check.tq;
+    p->tk = check.tk;
+    p->rows = check.rows;
+    p->batch = check.batch;
+    p->num_heads = check.num_heads;
+    p->causal = check.causal;
+    p->splits = check.splits;
+    p->max_kv_len = check.max_kv_len;
+    p->paged = check.paged;
+    p->planned = true;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t rows = tq * num_heads;
-    float* part_o = nullptr;
-    float* part_lse = nullptr;
-    if (splits > 1) {
-        const size_t need = static_cast<size_t>(splits) * static_cast<size_t>(rows) *
-                            (MLA_LATENT_DIM + 1) * sizeof(float);
-        if (st->part != nullptr && (st->part_bytes < need || st->part_device != dev)) {
-            // the previous call on this stream may still be using it
-            if (st->part_device == dev) {
-                e = hipStreamSynchronize(s);
-                if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            }
-            (void)hipFree(st->part);
-            st->part = nullptr;
-            st->part_bytes = 0;
-        }
-        if (st->part == nullptr) {
-            e = hipMalloc(&st->part, need);
-            if (e != hipSuccess) {
-                st->part = nullptr;
-                return fail(MLA_ENOMEM, "hipMalloc of the KV-split partial states failed");
-            }
-            st->part_bytes = need;
-            st->part_device = dev;
-        }
-        part_o = static_cast<float*>(st->part);
-        part_lse = part_o + static_cast<size_t>(splits) * rows * MLA_LATENT_DIM;
-    }
-    if (int r = st->dwl.upload(st->items, s)) return r;
-    e = mla::launch_prefill_absorbed(st->dwl.dev, static_cast<int64_t>(st->items.size()), q, kv,
-                                     out, lse, num_heads, sm_scale, s, pg, part_o, part_lse, rows);
-    if (e != hipSuccess) return hip_fail(e, "absorbed prefill kernel launch");
-    if (splits > 1) {
-        e = mla::launch_merge_splits(part_o, part_lse, splits, rows, out, lse, s);
-        if (e != hipSuccess) return hip_fail(e, "KV-split merge kernel launch");
-    }
-    return MLA_OK;
+    if (int r = absorbed_upload(p, s)) return r;
+    return absorbed_run(p, q, kv, sm_scale, out, lse, s, pg);
 }
 
 }  // namespace
@@ -640,6 +732,54 @@ int mla_absorbed_plan_items(const int32_t* qo_indptr, const int32_t* kv_indptr, 
         return fail(MLA_EINVAL, "capacity too small for the work list");
     if (!items.empty()) std::memcpy(dst, items.data(), items.size() * sizeof(mla::LatentItem));
     static_assert(sizeof(mla::LatentItem) == 12 * sizeof(int32_t), "12 int32 per item");
+    return MLA_OK;
+}
+
+int mla_absorbed_plan_create(mla_absorbed_plan** out) {
+    if (out == nullptr) return fail(MLA_EINVAL, "out is NULL");
+    *out = new (std::nothrow) mla_absorbed_plan();
+    if (*out == nullptr) return fail(MLA_ENOMEM, "absorbed plan");
+    return MLA_OK;
+}
+
+void mla_absorbed_plan_destroy(mla_absorbed_plan* plan) { delete plan; }
+
+int mla_absorbed_plan_build(mla_absorbed_plan* plan, const int32_t* qo_indptr,
+                            const int32_t* kv_indptr, int32_t batch, int32_t num_heads,
+                            int32_t causal, int32_t paged) {
+    if (paged != 0 && paged != 1) return fail(MLA_EINVAL, "paged must be 0 or 1");
+    return absorbed_build(plan, qo_indptr, kv_indptr, batch, num_heads, causal, paged != 0);
+}
+
+int mla_absorbed_plan_upload(mla_absorbed_plan* plan, void* stream) {
+    return absorbed_upload(plan, static_cast<hipStream_t>(stream));
+}
+
+int mla_absorbed_run(const mla_absorbed_plan* plan, const void* q, const void* kv, float sm_scale,
+                     void* out, float* lse, void* stream) {
+    return absorbed_run(plan, q, kv, sm_scale, out, lse, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int mla_absorbed_run_paged(const mla_absorbed_plan* plan, const void* q, const void* kv_cache,
+                           const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                           int32_t num_pages, float sm_scale, void* out, float* lse,
+                           void* stream) {
+    if (page_size < 32 || page_size % 32 != 0)
+        return fail(MLA_EINVAL, "page_size must be a positive multiple of 32");
+    if (max_pages < 1 || num_pages < 1) return fail(MLA_EINVAL, "max_pages and num_pages must be >= 1");
+    if (plan != nullptr && plan->batch > 0 &&
+        (block_table == nullptr || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))
+        return fail(MLA_EINVAL, "block_table must be non-NULL and 4-byte aligned");
+    const mla::PagedKv pg{block_table, max_pages, page_size, num_pages};
+    return absorbed_run(plan, q, kv_cache, sm_scale, out, lse, static_cast<hipStream_t>(stream),
+                        &pg);
+}
+
+int mla_absorbed_plan_info(const mla_absorbed_plan* plan, int64_t* n_items, int32_t* splits) {
+    if (plan == nullptr) return fail(MLA_EINVAL, "plan is NULL");
+    if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
+    if (n_items != nullptr) *n_items = static_cast<int64_t>(plan->items.size());
+    if (splits != nullptr) *splits = plan->splits;
     return MLA_OK;
 }
 

@@ -488,9 +488,24 @@ namespace {
 // keys, merged with the same log-sum-exp weights as merge_state):
 //   lse = ln sum_s e^lse_s,  o = sum_s e^(lse_s - lse) o_s;
 // splits with lse = -inf carry weight 0; all -inf gives o = 0, lse = -inf.
-// One row per 128 lanes, 4 dims per lane (16-byte loads of each partial).
+// One row per 128 lanes (two waves), 4 dims per lane. Each wave reads the
+// row's split LSEs in parallel (lane s takes split s) and reduces them with
+// cross-lane operations; the weights are then broadcast from their lanes,
+// and the partial rows are read a few splits at a time so that several
+// 16-byte loads are in flight.
 constexpr int kMergeThreads = 256;
 constexpr int kMaxSplits = 64;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
 
 __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
@@ -498,19 +513,29 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
     const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
     if (row >= rows) return;
     const int c = threadIdx.x & 127;
-    float mx = -INFINITY;
-    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[(int64_t)s * rows + row]);
+    const int lane = threadIdx.x & 63;
+    const float ls = lane < splits ? part_lse[(int64_t)lane * rows + row] : -INFINITY;
+    const float mx = wave_max(ls);
+    const float w = (mx == -INFINITY || ls == -INFINITY)
+                        ? 0.0f
+                        : __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);
+    const float sum = wave_sum(w);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float sum = 0.f;
-    if (mx != -INFINITY) {
-        for (int s = 0; s < splits; ++s) {
-            const float ls = part_lse[(int64_t)s * rows + row];
-            if (ls == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part_o + ((int64_t)s * rows + row) * kDv + c * 4);
-            acc += w * v;
-            sum += w;
+    const float* src = part_o + row * kDv + c * 4;
+    const int64_t split_stride = rows * kDv;
+    constexpr int kBatch = 4;
+    for (int s0 = 0; s0 < splits; s0 += kBatch) {
+        f32x4_t v[kBatch];
+        float ws[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int sk = s0 + k < splits ? s0 + k : splits - 1;
+            ws[k] = s0 + k < splits ? __shfl(w, sk) : 0.0f;
+            v[k] = ws[k] != 0.0f ? *reinterpret_cast<const f32x4_t*>(src + sk * split_stride)
+                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) acc += ws[k] * v[k];
     }
     const float inv = sum > 0.f ? 1.0f / sum : 0.0f;
     bf16x4_t o4;

@@ -372,7 +372,9 @@ def test_absorbed_partition_splits_keys_when_tiles_are_few():
     # a decode step (one token per sequence) over long prefixes: the keys of
     # each tile are shared out over several items
     _, _, splits = _check_latent_plan([1] * 16, [4096] * 16, 128, True)
-    assert splits == 8
+    assert splits == 16              # 16 tiles -> 256 items, one per CU
+    _, _, splits = _check_latent_plan([1] * 64, [4096] * 64, 128, True)
+    assert splits == 4
     _, _, splits = _check_latent_plan([1] * 4, [200, 37, 300, 1], 128, True)
     assert 1 < splits <= 2           # at least four 32-key tiles per split
     _, _, splits = _check_latent_plan([1] * 4, [64, 37, 100, 1], 128, False)
@@ -429,3 +431,28 @@ def test_absorbed_paged_rejects_invalid_arguments_before_any_hip_call():
     assert call(table=None) == 1
     assert call(table=bt.ctypes.data + 2) == 1        # misaligned table
     assert call(kvp=np.array([0, 65], dtype=np.int32)) == 1   # context > max_pages x page_size
+
+
+def test_absorbed_plan_states_and_info_without_a_gpu():
+    import ctypes
+    lib = mra.lib()
+    p = mra.AbsorbedPlan()
+    # not built: every run is a state error, before any HIP call
+    assert lib.mla_absorbed_run(p._h, 16, 16, 0.1, 16, 16, None) == 5
+    assert lib.mla_absorbed_plan_info(p._h, None, None) == 5
+    qo = np.array([0, 1, 2], dtype=np.int32)
+    kv = np.array([0, 4096, 8192], dtype=np.int32)
+    p.plan(qo, kv, 128, True)
+    info = p.info()
+    assert info["kv_splits"] > 1 and info["n_items"] % 8 == 0
+    # built, not uploaded
+    assert lib.mla_absorbed_run(p._h, 16, 16, 0.1, 16, 16, None) == 5
+    # built for a contiguous cache: a paged run is a state error
+    bt = np.zeros(4, dtype=np.int32)
+    assert lib.mla_absorbed_run_paged(p._h, 16, 16, bt.ctypes.data, 128, 32, 256, 0.1, 16, 16,
+                                      None) == 5
+    assert lib.mla_absorbed_run_paged(p._h, 16, 16, bt.ctypes.data, 128, 48, 256, 0.1, 16, 16,
+                                      None) == 1          # page size
+    with pytest.raises(RuntimeError):
+        p.plan([0, 3, 2], [0, 1, 2], 4, True)              # decreasing indptr
+    assert lib.mla_absorbed_plan_build(p._h, qo.ctypes.data, kv.ctypes.data, 2, 4, 1, 2) == 1

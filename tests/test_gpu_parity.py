@@ -634,3 +634,28 @@ def test_absorbed_paged_decode_matches_contiguous():
                                       True, x.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_absorbed_plan_run_matches_one_shot():
+    # plan once, run per layer: bit-identical to the one-shot call, for a
+    # prefill batch and for a decode batch with KV splits, contiguous and paged
+    for qo, kv, heads, seed in (([5, 130, 33], [5, 130, 300], 16, 60), ([1] * 6, [900] * 6, 128, 61)):
+        x = workloads.absorbed_inputs(qo, kv, heads, seed=seed, causal=True)
+        q, c = x.q.to(DEV), x.kv.to(DEV)
+        plan = mra.AbsorbedPlan().plan(x.qo_indptr, x.kv_indptr, heads, True).upload()
+        ref_o, ref_l = mra.absorbed_prefill(q, c, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+        for layer in range(2):
+            o, l = plan.run(q, c, x.sm_scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o, ref_o) and torch.equal(l, ref_l), f"layer {layer}"
+        pool, table = _latent_paged_cache(x, 64, extra_pages=2, seed=seed)
+        pplan = mra.AbsorbedPlan().plan(x.qo_indptr, x.kv_indptr, heads, True, paged=True).upload()
+        o, l = pplan.run_paged(q, pool.to(DEV), table.to(DEV), x.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    # a second layer's inputs through the same plan
+    x2 = workloads.absorbed_inputs([1] * 6, [900] * 6, 128, seed=62, causal=True)
+    o, l = plan.run(x2.q.to(DEV), x2.kv.to(DEV), x2.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.absorbed(x2.q, x2.kv, x2.qo_indptr, x2.kv_indptr, True, x2.sm_scale)
+    check(o, l, ro, rl, torch.bfloat16, "absorbed plan, second layer")
