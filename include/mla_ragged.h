@@ -26,6 +26,13 @@
  *   of the scaled logits);  O = sum_{j in J} exp(s_j - LSE) v_j.
  *   A row with J empty gets O = 0 and LSE = -inf.
  *
+ * Around that prefill the library exports, each declared below with its
+ * passage: the plan-once / run-per-layer form, a paged K/V form, a form
+ * planned on the device (graph-capturable), merge_state for chunked prefill,
+ * the KV decompression that feeds the MHA pass, and the weight-absorbed form
+ * that attends the 576-dim latent cache directly (one shared cache row per
+ * key, 512-dim values; prefill, paged prefix and decode).
+ *
  * Conventions for every entry point:
  *  - Tensors are dense, row-major, device pointers unless marked HOST.
  *    q [Tq, H, 192], k [Tk, H, 192], v [Tk, H, 128], out [Tq, H, 128]
