@@ -588,7 +588,8 @@ int mla_plan_items(const mla_plan* plan, int32_t* dst, int64_t capacity_items) {
     if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
     if (capacity_items < static_cast<int64_t>(plan->items.size()))
         return fail(MLA_EINVAL, "capacity is smaller than the item count");
-    std::memcpy(dst, plan->items.data(), plan->items.size() * sizeof(WorkItem));
+    if (!plan->items.empty())
+        std::memcpy(dst, plan->items.data(), plan->items.size() * sizeof(WorkItem));
     return MLA_OK;
 }
 
