@@ -101,8 +101,10 @@ const char *mla_version(void);
  *   lse          device fp32 [Tq, H] natural log, or NULL to skip it.
  *
  * Scratch: the work list lives in a library-owned, grow-only device buffer
- * kept per stream (plus pinned host staging), so calls on different streams
- * do not share it. Calls on one stream are ordered by that stream.
+ * kept per (device, stream) (plus pinned host staging), so calls on different
+ * streams do not share it. Calls on one stream are ordered by that stream;
+ * threads that share a stream are serialised on the host from planning to
+ * launch, so they may call concurrently.
  */
 int mla_ragged_prefill(const void *q, const void *k, const void *v,
                        const int32_t *qo_indptr, const int32_t *kv_indptr,
@@ -302,10 +304,11 @@ int mla_decompress_kv(const void *c_kv, const void *k_rope, const void *w_uk, co
  *   out   device bf16 [Tq, H, 512];  lse device fp32 [Tq, H] or NULL.
  *   All device pointers 16-byte aligned. The call plans on the host (the
  *   work list is kept per (device, stream) and reused) and enqueues one
- *   kernel on `stream`; it returns before the kernel ends. Calls on one
- *   stream must come from one thread at a time. When the row tiles alone
+ *   kernel on `stream`; it returns before the kernel ends. Threads that
+ *   share a stream are serialised on the host from planning to launch. When
+ *   the row tiles alone
  *   cannot fill the GPU (e.g. a decode step, one token per sequence), the
- *   keys of each tile are split over up to 8 work items (flash-decoding
+ *   keys of each tile are split over up to 32 work items (flash-decoding
  *   style); their fp32 partial states go to a library-owned, grow-only
  *   buffer per (device, stream) and a second kernel merges them.
  */

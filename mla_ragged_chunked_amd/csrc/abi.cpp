@@ -138,6 +138,7 @@ struct mla_plan {
     bool planned = false;
     bool uploaded = false;
     DeviceWorkList<WorkItem> dwl;
+    std::mutex oneshot_mu;        // one-shot calls sharing this (device, stream) plan
 };
 
 struct mla_absorbed_plan {
@@ -148,6 +149,7 @@ struct mla_absorbed_plan {
     bool planned = false;
     bool uploaded = false;
     DeviceWorkList<mla::LatentItem> dwl;
+    std::mutex oneshot_mu;        // one-shot calls sharing this (device, stream) plan
     // fp32 partial states of the KV splits (grow-only)
     void* part = nullptr;
     size_t part_bytes = 0;
@@ -297,9 +299,9 @@ int oneshot(const void* q, const void* k, const void* v, const int32_t* qo_indpt
             p = it->second;
         }
     }
-    // Calls on one stream are serialised by the caller's stream order; the
-    // host-side plan object is per (device, stream), so a thread per stream
-    // never shares it.
+    // The device side is ordered by the stream; threads that share the
+    // stream take turns on its plan from here to the launch.
+    std::lock_guard<std::mutex> plan_lock(p->oneshot_mu);
     p->items.swap(scratch_check.items);
     p->tq = scratch_check.tq;
     p->tk = scratch_check.tk;
@@ -488,7 +490,9 @@ int absorbed_call(const void* q, const void* kv, const int32_t* qo_indptr,
             p = it->second;
         }
     }
-    // the work list moves into the per-stream plan; its device buffers stay
+    // the work list moves into the per-stream plan; its device buffers stay.
+    // Threads that share the stream take turns on the plan up to the launch.
+    std::lock_guard<std::mutex> plan_lock(p->oneshot_mu);
     p->items.swap(check.items);
     p->tq = check.tq;
     p->tk = check.tk;

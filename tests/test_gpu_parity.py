@@ -318,6 +318,44 @@ def test_one_shot_on_two_streams():
         assert torch.equal(o, ref) and torch.equal(l, ref_l)
 
 
+def test_one_shot_threads_sharing_a_stream():
+    """Threads that enqueue one-shot calls on one stream take turns on its
+    plan: every result equals the same call made alone."""
+    import threading
+    cases = [_to(workloads.ragged_inputs(lens, lens, 2, torch.bfloat16, seed=60 + i), DEV)
+             for i, lens in enumerate(([300, 17], [64] * 5, [1, 2, 700], [129, 255, 33, 8]))]
+    refs = []
+    for x in cases:
+        refs.append(mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, True, x.sm_scale))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    results = [[] for _ in cases]
+    errors = []
+
+    def work(i):
+        try:
+            x = cases[i]
+            with torch.cuda.stream(stream):
+                for _ in range(6):
+                    results[i].append(mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr,
+                                                         True, x.sm_scale))
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    _flush("[gpu] one-shot prefill from 4 threads on one stream")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (ro, rl), outs in zip(refs, results):
+        assert len(outs) == 6
+        for o, l in outs:
+            assert torch.equal(o, ro) and torch.equal(l, rl)
+
+
 def test_native_library_is_loaded():
     with open("/proc/self/maps") as fh:
         maps = fh.read()
@@ -659,3 +697,43 @@ def test_absorbed_plan_run_matches_one_shot():
     torch.cuda.synchronize()
     ro, rl = oracle.absorbed(x2.q, x2.kv, x2.qo_indptr, x2.kv_indptr, True, x2.sm_scale)
     check(o, l, ro, rl, torch.bfloat16, "absorbed plan, second layer")
+
+
+def test_absorbed_one_shot_threads_sharing_a_stream():
+    """Decode batches (KV splits, so the per-stream split buffer is shared)
+    and a prefill batch from several threads on one stream: every result
+    equals the same call made alone."""
+    import threading
+    shapes = (([1] * 4, [700, 33, 2100, 5]), ([1] * 8, [1500] * 8), ([40, 130], [40, 400]))
+    cases = [workloads.absorbed_inputs(qo, kv, 16, seed=70 + i, causal=True)
+             for i, (qo, kv) in enumerate(shapes)]
+    dev = [(x.q.to(DEV), x.kv.to(DEV)) for x in cases]
+    refs = [mra.absorbed_prefill(q, c, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+            for x, (q, c) in zip(cases, dev)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    results = [[] for _ in cases]
+    errors = []
+
+    def work(i):
+        try:
+            x, (q, c) = cases[i], dev[i]
+            with torch.cuda.stream(stream):
+                for _ in range(5):
+                    results[i].append(mra.absorbed_prefill(q, c, x.qo_indptr, x.kv_indptr, True,
+                                                           x.sm_scale))
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    _flush("[gpu] one-shot absorbed calls from 3 threads on one stream")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (ro, rl), outs in zip(refs, results):
+        assert len(outs) == 5
+        for o, l in outs:
+            assert torch.equal(o, ro) and torch.equal(l, rl)
