@@ -626,6 +626,14 @@ def main():
         sec["device_plan"] = time_device_plan(mra, torch, x, args.steps, args.warmup)
         del x
         torch.cuda.empty_cache()
+        log("secondary: one GPU's share of an 8-way head split ...")
+        xh = workloads.deepseek_v3_batch(device="cuda", num_heads=16)
+        sec["head_shard_h16"] = time_workload_prefill(
+            mra, torch, xh, args.steps, 1,
+            "deepseek_v3_batch at 16 heads: one GPU's share when its 128 heads are split "
+            "over 8 GPUs (same sequences, same kernel)")
+        del xh
+        torch.cuda.empty_cache()
         log("secondary: chunked prefill ...")
         sec["chunked_prefill"] = time_chunked(mra, torch, workloads, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
