@@ -87,6 +87,15 @@ def test_ragged_qo_kv_mismatch_and_empty_sequences(dtype, causal):
     _flush(f"    max errors O={err[0]:.2e} LSE={err[1]:.2e}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_single_head(dtype, causal):
+    # H = 1: consecutive key rows are adjacent (384 B apart)
+    lens = [1, 130, 33, 257]
+    x = workloads.ragged_inputs(lens, [2 * n for n in lens], 1, dtype, seed=64, causal=causal)
+    _full_parity(x, f"one head dtype={dtype} causal={causal}")
+
+
 def test_single_visible_key_is_exact_in_bf16():
     x = workloads.ragged_inputs([3, 300, 64], [3, 300, 64], 8, torch.bfloat16, seed=33)
     g = _to(x, DEV)
