@@ -23,15 +23,14 @@
 //    MFMAs issue back to back), and transposing reads (ds_read_b64_tr_b16) of
 //    its first 512 dims are the V^T operand of O^T = V^T P^T (16 dv blocks x
 //    2 k-steps). LDS fragments are read four MFMAs ahead of use.
-//  * LDS read bandwidth, not the matrix cores, bounds this kernel: each wave
-//    reads the whole tile (36 KB as 16-byte rows, 32 KB through transposing
-//    reads at about half that rate) for its 32 rows. The chunk swizzle keeps
-//    both read kinds free of bank conflicts on the 64-bank LDS.
-//  * PV is deferred by one tile: iteration j computes the scores of tile j,
-//    then PV of tile j-1 (independent MFMAs) next to the softmax of tile j
-//    (VALU), so one wave alone keeps the matrix cores busy. A tile's stage
-//    therefore lives two iterations; the 4-stage ring (144 KB) issues tile
-//    j+2 into tile j-2's stage.
+//  * Each wave reads the whole tile (36 KB as 16-byte rows, 32 KB through
+//    transposing reads) for its 32 rows; the chunk swizzle keeps both read
+//    kinds free of bank conflicts on the 64-bank LDS. One wave per SIMD
+//    issues all of its MFMAs, LDS reads and softmax in order, which is what
+//    bounds the kernel (not the LDS bandwidth nor the matrix cores).
+//  * Iteration j computes the scores, softmax and PV of tile j, so a tile's
+//    stage is free again at the next barrier: the 4-stage ring (144 KB) keeps
+//    tiles j+1 .. j+3 in flight.
 //  * Online softmax in base 2, lazy rescale (threshold 2^8) and the row sum
 //    from the bf16-rounded p, as in the MHA kernel. The rare O rescale runs in
 //    place on the AGPRs.
@@ -337,11 +336,10 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     };
 
     // ---- pipeline ----
-    // Iteration j: wait for tile j (tile j+1 may still be in flight), barrier
-    // (retires tile j-2), issue tile j+2 into tile j-2's stage, scores of
-    // tile j, then the softmax of tile j (against the new running maximum)
-    // interleaved with PV of tile j-1 (whose P was taken against the old
-    // one), and last, if the maximum moved, O *= 2^(m_old - m_new).
+    // Iteration j: wait for tile j (tiles j+1 and j+2 may still be in
+    // flight), barrier (retires tile j-1), issue tile j+3 into tile j-1's
+    // stage, scores of tile j, the running maximum (O *= 2^(m_old - m_new)
+    // if it moved), the softmax of tile j and its PV.
     // the item's keys [kv_lo, kv_hi) as tiles 0 .. n_tiles-1 (kv_lo is a
     // multiple of 32); n_full: tiles every row of the wave sees whole,
     // n_wave: tiles with a key some row of the wave sees
@@ -365,22 +363,23 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
         }
     };
     auto sync_top = [&](int j) __attribute__((always_inline)) {
-        if (j + 1 < n_tiles) wait_vmcnt<kLoadsPerTile>();
+        if (j + 2 < n_tiles) wait_vmcnt<2 * kLoadsPerTile>();
+        else if (j + 1 < n_tiles) wait_vmcnt<kLoadsPerTile>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (j + 2 < n_tiles) issue_next(j + 2);
+        if (j + 3 < n_tiles) issue_next(j + 3);
     };
-    for (int t = 0; t < 2 && t < n_tiles; ++t) issue_next(t);
+    for (int t = 0; t < 3 && t < n_tiles; ++t) issue_next(t);
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) qf[s] = q_src[2 * s];
     // s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their maxima): Q and
     // the first tiles have all landed
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
 
-    bf16x8_t pprev[2];
     int j = 0;
-    auto iteration = [&](int jj, auto with_pv, auto masked) __attribute__((always_inline)) {
-        constexpr bool kPv = decltype(with_pv)::value;
+    // with_o: O may already hold earlier tiles (false for the first one)
+    auto iteration = [&](int jj, auto with_o, auto masked) __attribute__((always_inline)) {
+        constexpr bool kO = decltype(with_o)::value;
         sync_top(jj);
         f32x16_t sacc;
         scores(jj, jj % kStages, masked, sacc);
@@ -392,26 +391,18 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
         const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
-        bf16x8_t pcur[2];
-        exp_part(sacc, pcur);
-        if constexpr (kPv) {
-            pv((jj - 1) % kStages, pprev);
-            // keeps the softmax above the rescale branch, in the PV region
-            asm volatile("" ::"v"(pcur[0]), "v"(pcur[1]), "v"(l_run));
-            // O is still zero before the first PV, so only later tiles rescale
+        if constexpr (kO) {
             if (__builtin_expect(moved, 0)) scale_o(alpha);
         }
-        pprev[0] = pcur[0];
-        pprev[1] = pcur[1];
+        bf16x8_t p[2];
+        exp_part(sacc, p);
+        pv(jj % kStages, p);
     };
     if (n_wave > 0) {
         if (n_full > 0) iteration(0, std::false_type{}, std::false_type{});
         else iteration(0, std::false_type{}, std::true_type{});
         for (j = 1; j < n_full; ++j) iteration(j, std::true_type{}, std::false_type{});
         for (; j < n_wave; ++j) iteration(j, std::true_type{}, std::true_type{});
-        // PV of the wave's last tile: its stage is refilled only two
-        // iterations from now
-        pv((n_wave - 1) % kStages, pprev);
     }
     // tiles only other waves need: barriers and loads
     for (; j < n_tiles; ++j) sync_top(j);
