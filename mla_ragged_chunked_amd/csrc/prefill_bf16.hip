@@ -223,24 +223,26 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         }
         const uint8_t* kb = kseq + (row0 * H + head) * (kDqk * 2);
         const uint8_t* vb = vseq + (row0 * H + head) * (kDvo * 2);
-        uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
+        auto issue = [&](const uint32_t (&off)[kKBlocksPerWave + kVBlocksPerWave]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < kKBlocksPerWave; ++j)
+                dma16(kb, off[j], ks + (wave * kKBlocksPerWave + j) * 1024);
+#pragma unroll
+            for (int j = 0; j < kVBlocksPerWave; ++j)
+                dma16(vb, off[kKBlocksPerWave + j], vs + (wave * kVBlocksPerWave + j) * 1024);
+        };
         if (key0 + kBN - 1 > last_key) {
             const int lim = last_key - key0;
+            uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
 #pragma unroll
             for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j) {
                 const int r = ld_row[j] < lim ? ld_row[j] : lim;
                 off[j] = (uint32_t)r * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
             }
+            issue(off);
         } else {
-#pragma unroll
-            for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j) off[j] = ld_off[j];
+            issue(ld_off);
         }
-#pragma unroll
-        for (int j = 0; j < kKBlocksPerWave; ++j)
-            dma16(kb, off[j], ks + (wave * kKBlocksPerWave + j) * 1024);
-#pragma unroll
-        for (int j = 0; j < kVBlocksPerWave; ++j)
-            dma16(vb, off[kKBlocksPerWave + j], vs + (wave * kVBlocksPerWave + j) * 1024);
     };
 
     // LDS offsets of this lane's K fragment (row l32, chunk 2s + g) for
