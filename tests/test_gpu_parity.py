@@ -96,6 +96,35 @@ def test_single_head(dtype, causal):
     _full_parity(x, f"one head dtype={dtype} causal={causal}")
 
 
+def _random_shape(rng):
+    """A small random ragged batch: 1-6 sequences, lengths 0-600 (some empty),
+    qo and kv drawn independently half of the time."""
+    batch = int(rng.integers(1, 7))
+    qo = [int(v) for v in rng.integers(0, 601, batch)]
+    if rng.random() < 0.5:
+        kv = list(qo)
+    else:
+        kv = [int(v) for v in rng.integers(0, 601, batch)]
+    for i in range(batch):
+        if rng.random() < 0.15:
+            qo[i] = 0
+        if rng.random() < 0.15:
+            kv[i] = 0
+    return qo, kv
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_ragged_batches(case):
+    import numpy as np
+    rng = np.random.default_rng(1000 + case)
+    qo, kv = _random_shape(rng)
+    heads = int(rng.choice([1, 2, 3, 5, 8]))
+    causal = bool(rng.random() < 0.6)
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    x = workloads.ragged_inputs(qo, kv, heads, dtype, seed=2000 + case, causal=causal)
+    _full_parity(x, f"random case {case}: qo {qo} kv {kv} H={heads} causal={causal} {dtype}")
+
+
 def test_single_visible_key_is_exact_in_bf16():
     x = workloads.ragged_inputs([3, 300, 64], [3, 300, 64], 8, torch.bfloat16, seed=33)
     g = _to(x, DEV)
@@ -531,6 +560,17 @@ def _absorbed_parity(x: workloads.AbsorbedInputs, what, rows=None):
         idx = torch.tensor(rows)
         o, lse = o[idx], lse[idx]
     return check(o, lse, ro, rl, torch.bfloat16, f"absorbed {what}")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_absorbed_random_ragged_batches(case):
+    import numpy as np
+    rng = np.random.default_rng(3000 + case)
+    qo, kv = _random_shape(rng)
+    heads = int(rng.choice([1, 4, 16, 32]))
+    causal = bool(rng.random() < 0.6)
+    x = workloads.absorbed_inputs(qo, kv, heads, seed=4000 + case, causal=causal)
+    _absorbed_parity(x, f"random case {case}: qo {qo} kv {kv} H={heads}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
