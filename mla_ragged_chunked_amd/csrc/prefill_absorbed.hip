@@ -340,7 +340,8 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     // flight), barrier (retires tile j-1), issue tile j+3 into tile j-1's
     // stage, scores of tile j, the running maximum (O *= 2^(m_old - m_new)
     // if it moved), the softmax of tile j and its PV.
-    // the item's keys [kv_lo, kv_hi) as tiles 0 .. n_tiles-1 (kv_lo is a
+    //
+    // The item's keys [kv_lo, kv_hi) are tiles 0 .. n_tiles-1 (kv_lo is a
     // multiple of 32); n_full: tiles every row of the wave sees whole,
     // n_wave: tiles with a key some row of the wave sees
     const int n_tiles = (it.kv_hi - it.kv_lo + kBN - 1) / kBN;
