@@ -456,3 +456,28 @@ def test_absorbed_plan_states_and_info_without_a_gpu():
     with pytest.raises(RuntimeError):
         p.plan([0, 3, 2], [0, 1, 2], 4, True)              # decreasing indptr
     assert lib.mla_absorbed_plan_build(p._h, qo.ctypes.data, kv.ctypes.data, 2, 4, 1, 2) == 1
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU fallback: every compute entry of the binding rejects tensors that
+    are not on the GPU before it reaches the library."""
+    import torch
+    t, h = 5, 2
+    q = torch.zeros((t, h, 192), dtype=torch.bfloat16)
+    k = torch.zeros((t, h, 192), dtype=torch.bfloat16)
+    v = torch.zeros((t, h, 128), dtype=torch.bfloat16)
+    ind = [0, t]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mra.ragged_prefill(q, k, v, ind, ind, True, 0.1)
+    o = torch.zeros((t, h, 128), dtype=torch.bfloat16)
+    l = torch.zeros((t, h), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mra.merge_state(o, l, o, l)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mra.decompress_kv(torch.zeros((t, 512), dtype=torch.bfloat16),
+                          torch.zeros((t, 64), dtype=torch.bfloat16),
+                          torch.zeros((512, h * 128), dtype=torch.bfloat16),
+                          torch.zeros((512, h * 128), dtype=torch.bfloat16), h)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mra.absorbed_prefill(torch.zeros((t, h, 576), dtype=torch.bfloat16),
+                             torch.zeros((t, 576), dtype=torch.bfloat16), ind, ind, True, 0.1)
