@@ -125,6 +125,13 @@ def test_random_ragged_batches(case):
     _full_parity(x, f"random case {case}: qo {qo} kv {kv} H={heads} causal={causal} {dtype}")
 
 
+def test_more_than_128_heads():
+    # H = 160: token rows 61,440 B apart, 32-bit per-lane offsets still small
+    lens = [70, 1, 200]
+    x = workloads.ragged_inputs(lens, lens, 160, torch.bfloat16, seed=65, causal=True)
+    _full_parity(x, "160 heads")
+
+
 def test_single_visible_key_is_exact_in_bf16():
     x = workloads.ragged_inputs([3, 300, 64], [3, 300, 64], 8, torch.bfloat16, seed=33)
     g = _to(x, DEV)
@@ -597,6 +604,13 @@ def test_absorbed_many_heads():
     lens = [3, 70, 40]
     x = workloads.absorbed_inputs(lens, lens, 128, seed=13, causal=True)
     _absorbed_parity(x, "128 heads")
+
+
+def test_absorbed_160_heads():
+    # 160 rows per token: 128-row tiles start mid-token
+    lens = [3, 40, 9]
+    x = workloads.absorbed_inputs(lens, [20, 40, 300], 160, seed=66, causal=True)
+    _absorbed_parity(x, "160 heads")
 
 
 def test_absorbed_scale_extremes():
