@@ -648,6 +648,9 @@ def main():
         sec["skewed_batch"] = time_workload_prefill(
             mra, torch, xs, max(3, args.steps // 4), 1,
             f"skewed_batch: 64 log-uniform lengths [16, 32768], {xs.qo_indptr[-1]} tokens, 128 heads")
+        # the lengths after the 262,144-token cap rule, as drawn
+        sec["skewed_batch"]["seq_lens"] = [xs.qo_indptr[i + 1] - xs.qo_indptr[i]
+                                           for i in range(len(xs.qo_indptr) - 1)]
         del xs
         torch.cuda.empty_cache()
         log("secondary: decompression + prefill ...")
