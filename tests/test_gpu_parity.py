@@ -347,6 +347,48 @@ def test_paged_context_pass_against_the_oracle():
     check(o, l, ro, rl, torch.bfloat16, "paged context pass")
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_entry_points_agree_on_random_batches(case):
+    # Every route into the prefill on the same random ragged batch: the
+    # one-shot call (checked against the oracle), a plan with 2-head items,
+    # a page pool through a block table and the device-planned call. The
+    # arithmetic per (row, head) is the same in all of them, so their
+    # outputs must equal the one-shot call's bit for bit.
+    import numpy as np
+    rng = np.random.default_rng(3000 + case)
+    qo, kv = _random_shape(rng)
+    heads = int(rng.choice([2, 4, 6]))
+    causal = bool(rng.random() < 0.6)
+    dtype = torch.float32 if case % 4 == 3 else torch.bfloat16
+    page = int(rng.choice([32, 64]))
+    x = workloads.ragged_inputs(qo, kv, heads, dtype, seed=4000 + case, causal=causal)
+    _flush(f"[gpu] entry points case {case}: qo {qo} kv {kv} H={heads} causal={causal} "
+           f"{dtype} page={page}")
+    g = _to(x, DEV)
+    ref_o, ref_l = mra.ragged_prefill(g.q, g.k, g.v, x.qo_indptr, x.kv_indptr, causal,
+                                      x.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, causal, x.sm_scale)
+    check(ref_o, ref_l, ro, rl, dtype, f"entry points case {case}")
+    p = mra.Plan(heads_per_item=2).plan(x.qo_indptr, x.kv_indptr, heads, causal, dtype).upload()
+    o, l = p.run(g.q, g.k, g.v, x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l), "2-head items"
+    kc, vc, table = _paged_cache(g, page, extra_pages=2, seed=case)
+    o, l = mra.ragged_prefill_paged(g.q, kc, vc, x.qo_indptr, x.kv_indptr, table, causal,
+                                    x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l), "paged"
+    tq, tk = x.qo_indptr[-1], x.kv_indptr[-1]
+    dp = mra.DevicePlan(len(qo), max(tq, 1), max(tk, 1), heads, dtype)
+    qo_d = torch.tensor(x.qo_indptr, dtype=torch.int32, device=DEV)
+    kv_d = torch.tensor(x.kv_indptr, dtype=torch.int32, device=DEV)
+    o, l = dp.run(g.q, g.k, g.v, qo_d, kv_d, causal, x.sm_scale)
+    torch.cuda.synchronize()
+    assert int(dp.invalid_flag().item()) == 0
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l), "device plan"
+
+
 def test_one_shot_on_two_streams():
     lens = [200, 90]
     x = _to(workloads.ragged_inputs(lens, lens, 2, torch.bfloat16, seed=38), DEV)
