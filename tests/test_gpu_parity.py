@@ -779,6 +779,49 @@ def test_absorbed_paged_decode_matches_contiguous():
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_absorbed_entry_points_agree_on_random_batches(case):
+    # The absorbed routes on one random batch: the one-shot call (checked
+    # against the oracle on sampled rows), a plan run twice and a page pool.
+    # Odd cases are decode steps (one token per request, 128 heads), where
+    # the planner splits the keys and a merge combines the partials.
+    import numpy as np
+    rng = np.random.default_rng(5000 + case)
+    if case % 2:
+        batch = int(rng.integers(1, 9))
+        qo = [1] * batch
+        kv = [int(v) for v in rng.integers(1, 3000, batch)]
+        heads, causal = 128, True
+    else:
+        qo, kv = _random_shape(rng)
+        heads = int(rng.choice([2, 8, 16]))
+        causal = bool(rng.random() < 0.6)
+    page = int(rng.choice([32, 64, 128]))
+    x = workloads.absorbed_inputs(qo, kv, heads, seed=6000 + case, causal=causal)
+    _flush(f"[gpu] absorbed entry points case {case}: qo {qo} kv {kv} H={heads} "
+           f"causal={causal} page={page}")
+    q, c = x.q.to(DEV), x.kv.to(DEV)
+    ref_o, ref_l = mra.absorbed_prefill(q, c, x.qo_indptr, x.kv_indptr, causal, x.sm_scale)
+    torch.cuda.synchronize()
+    n_tok = x.qo_indptr[-1]
+    rows = sorted(set(int(r) for r in rng.integers(0, max(n_tok, 1), min(n_tok, 48))))
+    if rows:
+        ro, rl = oracle.absorbed(x.q, x.kv, x.qo_indptr, x.kv_indptr, causal, x.sm_scale,
+                                 rows=rows)
+        idx = torch.tensor(rows)
+        check(ref_o[idx], ref_l[idx], ro, rl, torch.bfloat16, f"absorbed entry points {case}")
+    plan = mra.AbsorbedPlan().plan(x.qo_indptr, x.kv_indptr, heads, causal).upload()
+    for layer in range(2):
+        o, l = plan.run(q, c, x.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), f"plan, layer {layer}"
+    pool, table = _latent_paged_cache(x, page, extra_pages=3, seed=case)
+    o, l = mra.absorbed_prefill_paged(q, pool.to(DEV), x.qo_indptr, x.kv_indptr, table.to(DEV),
+                                      causal, x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l), "paged"
+
+
 def test_absorbed_plan_run_matches_one_shot():
     # plan once, run per layer: bit-identical to the one-shot call, for a
     # prefill batch and for a decode batch with KV splits, contiguous and paged
