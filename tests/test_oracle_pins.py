@@ -415,3 +415,26 @@ def test_absorbed_equals_mha_over_a_broadcast_cache():
     v = kv[:, None, :512].expand(-1, 2, -1).contiguous()
     mo, ml = oracle.prefill(q, k, v, qo, kvi, True, scale)
     assert torch.allclose(o, mo, atol=1e-12, rtol=0) and torch.allclose(lse, ml, atol=1e-12, rtol=0)
+
+
+def test_weight_absorption_identity_links_the_two_mla_forms():
+    # MHA over the decompressed cache (K = [c_kv W_UK_h | k_rope], V = c_kv W_UV_h)
+    # equals the absorbed form: queries q_abs = [q_nope W_UK_h^T | q_rope] over
+    # the latent rows [c_kv | k_rope], whose 512-dim output is then projected by
+    # W_UV_h. Same scores (associativity of the products), so the same LSE.
+    heads, lens = 2, [5, 9]
+    c_kv, k_rope, w_uk, w_uv = _decomp_small(57, heads=heads, t=sum(lens))
+    g = torch.Generator().manual_seed(58)
+    q = workloads.randn((sum(lens), heads, DQK), g, torch.float32, "cpu").double()
+    ind = workloads.indptr_from_lengths(lens)
+    scale = 0.09
+    k, v = oracle.decompress(c_kv, k_rope, w_uk, w_uv, heads)
+    mo, ml = oracle.prefill(q, k, v, ind, ind, True, scale)
+    wk = w_uk.double().view(512, heads, 128)
+    wv = w_uv.double().view(512, heads, 128)
+    q_abs = torch.cat([torch.einsum("thd,chd->thc", q[:, :, :128], wk), q[:, :, 128:]], dim=-1)
+    lat = torch.cat([c_kv.double(), k_rope.double()], dim=-1)
+    ao, al = oracle.absorbed(q_abs.contiguous(), lat, ind, ind, True, scale)
+    o = torch.einsum("thc,chd->thd", ao, wv)
+    assert torch.allclose(al, ml, atol=1e-10, rtol=0)
+    assert torch.allclose(o, mo, atol=1e-10, rtol=0)
