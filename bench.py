@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (published: 2.5 PFLOP/s dense)
 PEAK_HBM_GBS = 8000.0         # HBM3E, 8 TB/s
+PEAK_FP32_TFLOPS = 157.3       # fp32 dense MFMA (published)
 
 
 def log(msg):
@@ -105,7 +106,8 @@ def parse():
                     help="target CPU time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
-    ap.add_argument("--only", choices=["merge", "decompress", "absorbed", "decode"], default=None,
+    ap.add_argument("--only", choices=["merge", "decompress", "absorbed", "decode", "fp32"],
+                    default=None,
                     help="run only one secondary kernel (for profiling) and print its figures")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; "
@@ -331,7 +333,7 @@ def time_paged_context(mra, torch, workloads, steps, warmup, page=64):
 
 
 def time_workload_prefill(mra, torch, x, steps, warmup, name):
-    plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, x.num_heads, x.causal).upload()
+    plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, x.num_heads, x.causal, x.q.dtype).upload()
     out = torch.empty((x.q.shape[0], x.num_heads, 128), dtype=x.q.dtype, device="cuda")
     lse = torch.empty((x.q.shape[0], x.num_heads), dtype=torch.float32, device="cuda")
     for _ in range(warmup):
@@ -347,6 +349,22 @@ def time_workload_prefill(mra, torch, x, steps, warmup, name):
     flops = 2.0 * x.num_heads * visible_pairs(x.qo_indptr, x.kv_indptr, x.causal) * 320
     return {"workload": name, "kernel_ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
             "flops": flops}
+
+
+def time_fp32_prefill(mra, torch, workloads, steps, warmup):
+    """The fp32 path (fp32 matrix-core kernel, no bf16 rounding) on the
+    DeepSeek-V3 lengths at 16 heads, against the fp32 dense MFMA peak."""
+    lens = workloads.deepseek_v3_lengths(2)
+    x = workloads.ragged_inputs(lens, lens, 16, torch.float32, seed=2, causal=True,
+                                device="cuda")
+    r = time_workload_prefill(mra, torch, x, steps, warmup,
+                              "deepseek_v3_batch lengths at 16 heads, fp32 inputs and outputs")
+    r["roofline"] = {"bound": "mfma", "achieved": r["TFLOP/s"], "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(r["TFLOP/s"] / PEAK_FP32_TFLOPS, 4),
+                     "traffic": profile_traffic("prefill_fp32_deepseek_v3_lengths_16heads.txt",
+                                                "mla_ragged_chunked_amd/csrc/prefill_fp32.hip"),
+                     "kernel": "prefill_fp32_kernel"}
+    return r
 
 
 def time_device_plan(mra, torch, x, steps, warmup):
@@ -574,6 +592,10 @@ def main():
         print(json.dumps(time_decompress(mra, torch, workloads, args.steps, args.warmup,
                                          with_prefill=False)), flush=True)
         return
+    if args.only == "fp32":
+        print(json.dumps(time_fp32_prefill(mra, torch, workloads, args.steps, args.warmup)),
+              flush=True)
+        return
     t0 = time.perf_counter()
     x = workloads.deepseek_v3_batch(device="cuda")
     torch.cuda.synchronize()
@@ -661,6 +683,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: absorbed decode step ...")
         sec["absorbed_decode"] = time_absorbed_decode(mra, torch, workloads, args.steps, 2)
+        torch.cuda.empty_cache()
+        log("secondary: fp32 prefill ...")
+        sec["fp32_prefill"] = time_fp32_prefill(mra, torch, workloads, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
         result["secondary"] = sec
     print(json.dumps(result), flush=True)

@@ -42,6 +42,7 @@ def test_visible_pairs_matches_a_brute_force_count(causal):
     ("prefill_absorbed_deepseek_v3_batch.txt", "mla_ragged_chunked_amd/csrc/prefill_absorbed.hip"),
     ("merge_state_16384x128_bf16.txt", "mla_ragged_chunked_amd/csrc/merge.hip"),
     ("decompress_kv_8x4096_128heads.txt", "mla_ragged_chunked_amd/csrc/decompress.hip"),
+    ("prefill_fp32_deepseek_v3_lengths_16heads.txt", "mla_ragged_chunked_amd/csrc/prefill_fp32.hip"),
 ])
 def test_committed_profiles_match_the_kernel_sources(profile, source):
     # the bench reports a kernel's measured traffic only while the profile's
