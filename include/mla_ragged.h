@@ -104,7 +104,8 @@ const char *mla_version(void);
  * kept per (device, stream) (plus pinned host staging), so calls on different
  * streams do not share it. Calls on one stream are ordered by that stream;
  * threads that share a stream are serialised on the host from planning to
- * launch, so they may call concurrently.
+ * launch, so they may call concurrently. Growing that buffer never waits
+ * for work on other streams (the outgrown buffer is kept, not freed).
  */
 int mla_ragged_prefill(const void *q, const void *k, const void *v,
                        const int32_t *qo_indptr, const int32_t *kv_indptr,
@@ -114,10 +115,12 @@ int mla_ragged_prefill(const void *q, const void *k, const void *v,
 /*
  * Paged K/V variant of mla_ragged_prefill: the keys and values come from
  * page-organised caches through a block table instead of contiguous [Tk, H, D]
- * buffers (how serving systems hold a request's prefix: the page pool and
- * block table of "[DeepseekR1] How ragged prefill manage kv_cache?", sglang
- * issue 3849, token_to_kv_pool; and the block_table / slot_mapping of
- * "[KVCache] PagedKVCache refactor, FlashInfer JIT and MLA integration").
+ * buffers (how serving systems hold a request's prefix: the token-to-KV pool
+ * of "[DeepseekR1] How ragged prefill manage kv_cache?", sglang issue 3849,
+ * token_to_kv_pool; and the per-request block table of the attention
+ * metadata on the vLLM page "vllm/models/deepseek_v4/sparse_mla.py",
+ * DeepseekV4FlashMLAMetadata.block_table, filled by the metadata builder's
+ * build()).
  *
  *   k_cache      device [num_pages, page_size, H, 192], dtype `dtype`.
  *   v_cache      device [num_pages, page_size, H, 128].
@@ -150,8 +153,10 @@ typedef struct mla_plan mla_plan;
 int mla_plan_create(mla_plan **out);
 
 /* Destroy a plan and free its host and device buffers. NULL is a no-op.
- * The caller must make sure no launched run still reads the plan (for
- * example by synchronising the stream it ran on). */
+ * Every run records an event on its stream; destroy first waits (on the
+ * host) for the plan's most recent run to finish, then frees, so a launched
+ * run never reads freed memory. Runs of one plan on several streams must be
+ * ordered by the caller (the last one launched is the one waited for). */
 void mla_plan_destroy(mla_plan *plan);
 
 /*
@@ -168,17 +173,27 @@ int mla_ragged_plan(mla_plan *plan, const int32_t *qo_indptr, const int32_t *kv_
 
 /* Copy the planned work list to the plan's device buffer (allocated or grown
  * on first use) with an asynchronous copy on `stream`, through pinned host
- * staging. Run the kernel on the same stream (or synchronise first). */
+ * staging. Run the kernel on the same stream (or synchronise first).
+ * A buffer outgrown by a larger work list is kept (not freed) until the plan
+ * is destroyed, since runs launched earlier may still read it: growing makes
+ * no device-wide synchronisation. The host waits only when all four pinned
+ * staging slots hold copies still in flight (for the oldest of them). */
 int mla_plan_upload(mla_plan *plan, void *stream);
 
 /*
  * Launch the prefill kernel for an uploaded plan. Tensors as for
- * mla_ragged_prefill; `dtype` must equal the planned dtype and the tensors
- * must match the planned indptrs (Tq = qo_indptr[batch], Tk = kv_indptr[batch],
- * num_heads), else MLA_ESTATE. Enqueues exactly one kernel.
+ * mla_ragged_prefill, with their sizes:
+ *   q_rows     rows of q and out (tokens); must equal the planned
+ *              qo_indptr[batch].
+ *   kv_rows    rows of k and v; must be >= the planned kv_indptr[batch].
+ *   num_heads  heads of q, k, v and out; must equal the planned num_heads.
+ * `dtype` must equal the planned dtype. Any mismatch returns MLA_ESTATE
+ * before a kernel is enqueued. Enqueues exactly one kernel, then records the
+ * plan's completion event on `stream`.
  */
 int mla_ragged_run(const mla_plan *plan, const void *q, const void *k, const void *v,
-                   float sm_scale, int32_t dtype, void *out, float *lse, void *stream);
+                   int64_t q_rows, int64_t kv_rows, int32_t num_heads, float sm_scale,
+                   int32_t dtype, void *out, float *lse, void *stream);
 
 /*
  * Work-list inspection (host only): item count, and a copy of the items as
@@ -209,7 +224,10 @@ int mla_plan_set_xcds(mla_plan *plan, int32_t n_xcd);
 int mla_plan_set_heads_per_item(mla_plan *plan, int32_t heads_per_item);
 
 /*
- * Device-planned prefill (for HIP graph capture and host-sync-free loops):
+ * Device-planned prefill (for HIP graph capture and host-sync-free loops;
+ * the workspace plays the part of the metadata buffers that the builder of
+ * "vllm/models/deepseek_v4/sparse_mla.py" pre-allocates in __init__ so their
+ * addresses stay fixed under CUDA-graph replay):
  * the same operation as mla_ragged_prefill, but qo_indptr and kv_indptr are
  * DEVICE int32 [batch+1] arrays read only by the GPU, and the work list is
  * built on the GPU into a caller-provided workspace. The call enqueues three
@@ -319,8 +337,9 @@ int mla_absorbed_prefill(const void *q, const void *kv, const int32_t *qo_indptr
 /*
  * Paged variant of mla_absorbed_prefill: the latent cache rows come from a
  * page pool through a block table (the absorb path of sglang issue 3849 runs
- * over a paged prefix held in the token-to-KV pool; block_table as in
- * "[KVCache] PagedKVCache refactor, FlashInfer JIT and MLA integration").
+ * over a paged prefix held in the token-to-KV pool; the block table as in
+ * the attention metadata of "vllm/models/deepseek_v4/sparse_mla.py",
+ * DeepseekV4FlashMLAMetadata.block_table).
  *
  *   kv_cache     device bf16 [num_pages, page_size, 576].
  *   block_table  DEVICE int32 [batch, max_pages]: key j of sequence b is slot
@@ -343,19 +362,25 @@ int mla_absorbed_prefill_paged(const void *q, const void *kv_cache, const int32_
  * Plan-once / run-per-layer form of the absorbed prefill (the plan()/run()
  * split of "vllm.v1.attention.backends.mla.prefill.flashinfer": the work list
  * depends only on the indptrs, so one plan serves every layer of a step).
- *   create / destroy  the plan object (destroy synchronises its device).
+ *   create / destroy  the plan object (destroy waits on the host for the
+ *            plan's most recent run, then frees its buffers).
  *   build    plans from HOST indptrs as mla_absorbed_prefill does (including
  *            the choice of KV splits); paged = 1 plans for run_paged.
  *   upload   copies the work list to the current device on `stream` and
- *            allocates the split buffer (a second upload after a rebuild may
- *            reallocate it, after synchronising the device).
+ *            allocates the split buffer (a larger one after a rebuild; the
+ *            outgrown buffer is kept until destroy, so no device-wide
+ *            synchronisation is needed).
  *   run      one kernel (plus the split merge) on `stream`: q, kv, out, lse
- *            as for mla_absorbed_prefill; run_paged as for
- *            mla_absorbed_prefill_paged.
+ *            as for mla_absorbed_prefill, with q_rows = rows of q and out
+ *            (must equal the planned qo_indptr[batch]), kv_rows = rows of kv
+ *            (must be >= the planned kv_indptr[batch]) and num_heads (must
+ *            equal the plan's); run_paged as for mla_absorbed_prefill_paged,
+ *            with q_rows and num_heads checked the same way.
  *   info     number of work items and KV splits.
  * Runs of one plan that uses KV splits share its split buffer: they must not
  * overlap (issue them on one stream, or order them). Errors: MLA_ESTATE when
- * the plan is not built/uploaded, or built for the other cache kind.
+ * the plan is not built/uploaded, built for the other cache kind, or the
+ * tensor sizes do not match it.
  */
 typedef struct mla_absorbed_plan mla_absorbed_plan;
 int mla_absorbed_plan_create(mla_absorbed_plan **out);
@@ -364,12 +389,13 @@ int mla_absorbed_plan_build(mla_absorbed_plan *plan, const int32_t *qo_indptr,
                             const int32_t *kv_indptr, int32_t batch, int32_t num_heads,
                             int32_t causal, int32_t paged);
 int mla_absorbed_plan_upload(mla_absorbed_plan *plan, void *stream);
-int mla_absorbed_run(const mla_absorbed_plan *plan, const void *q, const void *kv, float sm_scale,
+int mla_absorbed_run(const mla_absorbed_plan *plan, const void *q, const void *kv,
+                     int64_t q_rows, int64_t kv_rows, int32_t num_heads, float sm_scale,
                      void *out, float *lse, void *stream);
 int mla_absorbed_run_paged(const mla_absorbed_plan *plan, const void *q, const void *kv_cache,
-                           const int32_t *block_table, int32_t max_pages, int32_t page_size,
-                           int32_t num_pages, float sm_scale, void *out, float *lse,
-                           void *stream);
+                           int64_t q_rows, int32_t num_heads, const int32_t *block_table,
+                           int32_t max_pages, int32_t page_size, int32_t num_pages,
+                           float sm_scale, void *out, float *lse, void *stream);
 int mla_absorbed_plan_info(const mla_absorbed_plan *plan, int64_t *n_items, int32_t *splits);
 
 /*

@@ -4,7 +4,10 @@
 // with no host synchronisation and no allocation. The pages plan on the host
 // once per batch ("vllm.v1.attention.backends.mla.prefill.flashinfer",
 // plan() inside finalize_attention_metadata); serving loops that replay
-// captured graphs need the plan to follow the indptrs on the device instead.
+// captured graphs need the plan to follow the indptrs on the device instead,
+// in buffers whose addresses stay fixed across replays (as the metadata
+// builder of "vllm/models/deepseek_v4/sparse_mla.py" pre-allocates its
+// metadata buffers in __init__ for CUDA-graph address stability).
 //
 // Order (same goals as the host partitioner, simpler rule):
 //  * Sequences are sorted by cost, heaviest first (cost of a sequence = sum
