@@ -24,9 +24,10 @@ import torch
 
 __all__ = ["ragged_prefill", "ragged_prefill_paged", "merge_state", "decompress_kv",
            "absorbed_prefill", "absorbed_prefill_paged", "absorbed_plan_items", "AbsorbedPlan", "Plan", "DevicePlan", "MlaError", "lib",
-           "LIB_PATH", "DQK", "DVO", "DLAT", "DROPE", "EXPORTED_SYMBOLS"]
+           "LIB_PATH", "DQK", "DVO", "DLAT", "DROPE", "PREFILL_BLOCK_M", "EXPORTED_SYMBOLS"]
 
 DQK, DVO, DLAT, DROPE = 192, 128, 512, 64
+PREFILL_BLOCK_M = 128          # query rows per work item of the bf16 prefill kernel
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla_ragged.so")
 _BF16, _FP32 = 0, 1
@@ -77,7 +78,7 @@ def lib():
         "mla_plan_destroy": ([P], None),
         "mla_ragged_plan": ([P, P, P, I32, I32, I32, I32], ctypes.c_int),
         "mla_plan_upload": ([P, P], ctypes.c_int),
-        "mla_ragged_run": ([P, P, P, P, F, I32, P, P, P], ctypes.c_int),
+        "mla_ragged_run": ([P, P, P, P, I64, I64, I32, F, I32, P, P, P], ctypes.c_int),
         "mla_plan_info": ([P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32),
                            ctypes.POINTER(I32)], ctypes.c_int),
         "mla_plan_items": ([P, P, I64], ctypes.c_int),
@@ -99,8 +100,9 @@ def lib():
         "mla_absorbed_plan_destroy": ([P], None),
         "mla_absorbed_plan_build": ([P, P, P, I32, I32, I32, I32], ctypes.c_int),
         "mla_absorbed_plan_upload": ([P, P], ctypes.c_int),
-        "mla_absorbed_run": ([P, P, P, F, P, P, P], ctypes.c_int),
-        "mla_absorbed_run_paged": ([P, P, P, P, I32, I32, I32, F, P, P, P], ctypes.c_int),
+        "mla_absorbed_run": ([P, P, P, I64, I64, I32, F, P, P, P], ctypes.c_int),
+        "mla_absorbed_run_paged": ([P, P, P, I64, I32, P, I32, I32, I32, F, P, P, P],
+                                   ctypes.c_int),
         "mla_absorbed_plan_info": ([P, ctypes.POINTER(I64), ctypes.POINTER(I32)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -202,8 +204,9 @@ class Plan:
         _dev_tensor(out, "out")
         _check_shapes(q, k, v, out, lse if return_lse else None)
         with torch.cuda.device(q.device):
-            _check(self._lib.mla_ragged_run(self._h, _ptr(q), _ptr(k), _ptr(v), float(sm_scale),
-                                            _DT[q.dtype], _ptr(out),
+            # the library checks the sizes against the plan (MLA_ESTATE)
+            _check(self._lib.mla_ragged_run(self._h, _ptr(q), _ptr(k), _ptr(v), tq, k.shape[0],
+                                            heads, float(sm_scale), _DT[q.dtype], _ptr(out),
                                             _ptr(lse) if return_lse else None,
                                             _stream(q.device)),
                    "mla_ragged_run")
@@ -582,7 +585,8 @@ class AbsorbedPlan:
             raise ValueError("kv must be bf16 [Tk,576]")
         out, lse = self._outputs(q, out, lse, return_lse)
         with torch.cuda.device(q.device):
-            _check(self._lib.mla_absorbed_run(self._h, _ptr(q), _ptr(kv), float(sm_scale),
+            _check(self._lib.mla_absorbed_run(self._h, _ptr(q), _ptr(kv), q.shape[0],
+                                              kv.shape[0], q.shape[1], float(sm_scale),
                                               _ptr(out), _ptr(lse) if return_lse else None,
                                               _stream(q.device)),
                    "mla_absorbed_run")
@@ -601,7 +605,8 @@ class AbsorbedPlan:
         out, lse = self._outputs(q, out, lse, return_lse)
         with torch.cuda.device(q.device):
             _check(self._lib.mla_absorbed_run_paged(
-                self._h, _ptr(q), _ptr(kv_cache), _ptr(block_table), block_table.shape[1],
+                self._h, _ptr(q), _ptr(kv_cache), q.shape[0], q.shape[1], _ptr(block_table),
+                block_table.shape[1],
                 kv_cache.shape[1], kv_cache.shape[0], float(sm_scale), _ptr(out),
                 _ptr(lse) if return_lse else None, _stream(q.device)),
                 "mla_absorbed_run_paged")

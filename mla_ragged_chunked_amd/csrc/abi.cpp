@@ -38,6 +38,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Pinned host staging + device buffer for one work list. Grow-only.
 // A ring of pinned slots lets several uploads be in flight on a stream
 // before the host has to wait for the oldest copy to finish.
+//
+// A buffer outgrown by a larger work list is retired, not freed: a run
+// launched earlier (on this or any stream) may still read it, and HIP's
+// hipFree / hipHostFree synchronise the whole device. Retired buffers are
+// freed in release() (plan destruction), after the owner has waited for the
+// plan's last run. Growth is geometric, so the retired buffers together stay
+// smaller than the live one.
 template <class Item>
 struct DeviceWorkList {
     static constexpr int kRing = 4;
@@ -49,9 +56,12 @@ struct DeviceWorkList {
     hipEvent_t done[kRing] = {};
     bool pending[kRing] = {};
     int next = 0;
+    std::vector<void*> retired_dev;
+    std::vector<void*> retired_pinned;
 
     ~DeviceWorkList() { release(); }
 
+    // Free everything. The caller has waited for every run that reads `dev`.
     void release() {
         for (int i = 0; i < kRing; ++i) {
             if (pending[i]) (void)hipEventSynchronize(done[i]);
@@ -62,13 +72,22 @@ struct DeviceWorkList {
             pinned_cap[i] = 0;
             pending[i] = false;
         }
+        for (void* p : retired_pinned) (void)hipHostFree(p);
+        retired_pinned.clear();
         if (dev) (void)hipFree(dev);
+        for (void* p : retired_dev) (void)hipFree(p);
+        retired_dev.clear();
         dev = nullptr;
         dev_cap = 0;
     }
 
-    // Asynchronously copy `items` to `dev` on `stream`.
-    int upload(const std::vector<Item>& items, hipStream_t stream) {
+    static size_t grown(size_t cap, size_t need) { return need > 2 * cap ? need : 2 * cap; }
+
+    // Asynchronously copy `items` to `dev` on `stream`. `before_release` is
+    // called (with the old device current) when the list moves to another
+    // device, so the owner can wait for its last run first.
+    template <class Wait>
+    int upload(const std::vector<Item>& items, hipStream_t stream, Wait before_release) {
         int cur = -1;
         hipError_t e = hipGetDevice(&cur);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -76,40 +95,49 @@ struct DeviceWorkList {
             // the plan moves to another device: drop the old buffers
             int keep = cur;
             (void)hipSetDevice(device);
+            before_release();
             release();
             (void)hipSetDevice(keep);
         }
         device = cur;
         const size_t n = items.empty() ? 1 : items.size();
         if (dev_cap < n) {
-            if (dev) {
-                // a previous run on some stream may still read the old buffer
-                e = hipDeviceSynchronize();
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-                (void)hipFree(dev);
-                dev = nullptr;
-                dev_cap = 0;
+            const size_t cap = grown(dev_cap, n);
+            Item* fresh = nullptr;
+            e = hipMalloc(&fresh, cap * sizeof(Item));
+            if (e != hipSuccess) return fail(MLA_ENOMEM, "hipMalloc of the work list failed");
+            try {
+                if (dev) retired_dev.push_back(dev);
+            } catch (const std::bad_alloc&) {
+                (void)hipFree(fresh);
+                return fail(MLA_ENOMEM, "host allocation of the retired-buffer list failed");
             }
-            e = hipMalloc(&dev, n * sizeof(Item));
-            if (e != hipSuccess) { dev = nullptr; return fail(MLA_ENOMEM, "hipMalloc of the work list failed"); }
-            dev_cap = n;
+            dev = fresh;
+            dev_cap = cap;
         }
         if (items.empty()) return MLA_OK;
         const int slot = next;
         next = (next + 1) % kRing;
         if (pending[slot]) {
+            // the copy four uploads ago used this slot: wait for that copy only
             e = hipEventSynchronize(done[slot]);
             if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
             pending[slot] = false;
         }
         if (pinned_cap[slot] < items.size()) {
-            if (pinned[slot]) (void)hipHostFree(pinned[slot]);
-            pinned[slot] = nullptr;
-            pinned_cap[slot] = 0;
-            e = hipHostMalloc(reinterpret_cast<void**>(&pinned[slot]), items.size() * sizeof(Item),
+            const size_t cap = grown(pinned_cap[slot], items.size());
+            Item* fresh = nullptr;
+            e = hipHostMalloc(reinterpret_cast<void**>(&fresh), cap * sizeof(Item),
                               hipHostMallocDefault);
-            if (e != hipSuccess) { pinned[slot] = nullptr; return fail(MLA_ENOMEM, "hipHostMalloc of staging failed"); }
-            pinned_cap[slot] = items.size();
+            if (e != hipSuccess) return fail(MLA_ENOMEM, "hipHostMalloc of staging failed");
+            try {
+                if (pinned[slot]) retired_pinned.push_back(pinned[slot]);
+            } catch (const std::bad_alloc&) {
+                (void)hipHostFree(fresh);
+                return fail(MLA_ENOMEM, "host allocation of the retired-buffer list failed");
+            }
+            pinned[slot] = fresh;
+            pinned_cap[slot] = cap;
         }
         if (!done[slot]) {
             e = hipEventCreateWithFlags(&done[slot], hipEventDisableTiming);
@@ -126,6 +154,43 @@ struct DeviceWorkList {
     }
 };
 
+// Completion of a plan's most recent run: recorded on the run's stream after
+// its kernels, waited for (on the host) only before the plan frees memory
+// that run may read. Waiting for it never waits for other work.
+struct RunFence {
+    hipEvent_t ev = nullptr;
+    int device = -1;
+    bool recorded = false;
+
+    int record(hipStream_t stream) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        if (ev != nullptr && device != cur) {
+            wait();
+            (void)hipEventDestroy(ev);
+            ev = nullptr;
+        }
+        if (ev == nullptr) {
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e != hipSuccess) { ev = nullptr; return hip_fail(e, "hipEventCreate"); }
+            device = cur;
+        }
+        e = hipEventRecord(ev, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        recorded = true;
+        return MLA_OK;
+    }
+    void wait() {
+        if (ev != nullptr && recorded) (void)hipEventSynchronize(ev);
+        recorded = false;
+    }
+    ~RunFence() {
+        wait();
+        if (ev != nullptr) (void)hipEventDestroy(ev);
+    }
+};
+
 }  // namespace
 
 struct mla_plan {
@@ -138,7 +203,13 @@ struct mla_plan {
     bool planned = false;
     bool uploaded = false;
     DeviceWorkList<WorkItem> dwl;
+    mutable RunFence last_run;    // recorded by every run
     std::mutex oneshot_mu;        // one-shot calls sharing this (device, stream) plan
+    ~mla_plan() {
+        // no launched run may still read the work list when it is freed
+        last_run.wait();
+        dwl.release();
+    }
 };
 
 struct mla_absorbed_plan {
@@ -149,20 +220,31 @@ struct mla_absorbed_plan {
     bool planned = false;
     bool uploaded = false;
     DeviceWorkList<mla::LatentItem> dwl;
+    mutable RunFence last_run;    // recorded by every run
     std::mutex oneshot_mu;        // one-shot calls sharing this (device, stream) plan
-    // fp32 partial states of the KV splits (grow-only)
+    // fp32 partial states of the KV splits (grow-only; an outgrown buffer is
+    // retired until destruction, like the work list's)
     void* part = nullptr;
     size_t part_bytes = 0;
     int part_device = -1;
+    std::vector<void*> retired_part;
+    void free_parts() {
+        if (part != nullptr) (void)hipFree(part);
+        for (void* q : retired_part) (void)hipFree(q);
+        part = nullptr;
+        part_bytes = 0;
+        retired_part.clear();
+    }
     ~mla_absorbed_plan() {
-        if (part != nullptr) {
+        last_run.wait();
+        if (part != nullptr || !retired_part.empty()) {
             int keep = -1;
             (void)hipGetDevice(&keep);
             (void)hipSetDevice(part_device);
-            (void)hipDeviceSynchronize();
-            (void)hipFree(part);
+            free_parts();
             (void)hipSetDevice(keep);
         }
+        dwl.release();
     }
 };
 
@@ -229,15 +311,22 @@ int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, in
     return MLA_OK;
 }
 
-int do_run(const mla_plan* p, const void* q, const void* k, const void* v, float sm_scale,
-           int32_t dtype, void* out, float* lse, hipStream_t stream,
-           const mla::PagedKv* paged = nullptr) {
+// q_rows / kv_rows / num_heads: the sizes of the tensors the caller passes
+// (kv_rows < 0: paged K/V, no contiguous key rows to check).
+int do_run(const mla_plan* p, const void* q, const void* k, const void* v, int64_t q_rows,
+           int64_t kv_rows, int32_t num_heads, float sm_scale, int32_t dtype, void* out,
+           float* lse, hipStream_t stream, const mla::PagedKv* paged = nullptr) {
     if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
     if (p->paged != (paged != nullptr))
         return fail(MLA_ESTATE, "plan and call disagree on paged K/V");
     if (!p->planned) return fail(MLA_ESTATE, "plan has not been built");
-    if (!p->uploaded) return fail(MLA_ESTATE, "plan has not been uploaded (mla_plan_upload)");
     if (dtype != p->dtype) return fail(MLA_ESTATE, "dtype differs from the planned dtype");
+    if (num_heads != p->num_heads) return fail(MLA_ESTATE, "num_heads differs from the plan");
+    if (q_rows != p->tq)
+        return fail(MLA_ESTATE, "q / out rows differ from the planned qo_indptr[batch]");
+    if (paged == nullptr && kv_rows < p->tk)
+        return fail(MLA_ESTATE, "k / v have fewer rows than the planned kv_indptr[batch]");
+    if (!p->uploaded) return fail(MLA_ESTATE, "plan has not been uploaded (mla_plan_upload)");
     if (int s = check_scale(sm_scale)) return s;
     if (int s = check_tensors(q, k, v, out, lse, p->tq, paged != nullptr ? 1 : p->tk)) return s;
     int cur = -1;
@@ -252,7 +341,7 @@ int do_run(const mla_plan* p, const void* q, const void* k, const void* v, float
             : mla::launch_prefill_fp32(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale,
                                        stream, paged);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
-    return MLA_OK;
+    return p->last_run.record(stream);
 }
 
 // One-shot calls keep one plan per (device, stream).
@@ -314,7 +403,8 @@ int oneshot(const void* q, const void* k, const void* v, const int32_t* qo_indpt
     p->planned = true;
     p->uploaded = false;
     if (int s = mla_plan_upload(p, stream)) return s;
-    return do_run(p, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream), paged);
+    return do_run(p, q, k, v, tq, paged != nullptr ? -1 : tk, num_heads, sm_scale, dtype, out,
+                  lse, static_cast<hipStream_t>(stream), paged);
 }
 
 // Weight-absorbed prefill: one-shot calls keep one plan per (device, stream).
@@ -389,39 +479,52 @@ int absorbed_upload(mla_absorbed_plan* p, hipStream_t stream) {
     if (p->splits > 1) {
         const size_t need = static_cast<size_t>(p->splits) * static_cast<size_t>(p->rows) *
                             (MLA_LATENT_DIM + 1) * sizeof(float);
-        if (p->part != nullptr && (p->part_bytes < need || p->part_device != dev)) {
-            // earlier runs of this plan may still be using it
+        if (p->part_device != -1 && p->part_device != dev) {
+            // the plan moves to another device: its last run must end first
+            p->last_run.wait();
             int keep = dev;
             (void)hipSetDevice(p->part_device);
-            e = hipDeviceSynchronize();
-            (void)hipFree(p->part);
+            p->free_parts();
             (void)hipSetDevice(keep);
-            p->part = nullptr;
-            p->part_bytes = 0;
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            p->part_device = -1;
         }
-        if (p->part == nullptr) {
-            e = hipMalloc(&p->part, need);
-            if (e != hipSuccess) {
-                p->part = nullptr;
+        if (p->part_bytes < need) {
+            // an earlier run may still use the old buffer: retire it
+            void* fresh = nullptr;
+            e = hipMalloc(&fresh, need);
+            if (e != hipSuccess)
                 return fail(MLA_ENOMEM, "hipMalloc of the KV-split partial states failed");
+            try {
+                if (p->part != nullptr) p->retired_part.push_back(p->part);
+            } catch (const std::bad_alloc&) {
+                (void)hipFree(fresh);
+                return fail(MLA_ENOMEM, "host allocation of the retired-buffer list failed");
             }
+            p->part = fresh;
             p->part_bytes = need;
             p->part_device = dev;
         }
     }
-    if (int r = p->dwl.upload(p->items, stream)) return r;
+    if (int r = p->dwl.upload(p->items, stream, [p] { p->last_run.wait(); })) return r;
     p->uploaded = true;
     return MLA_OK;
 }
 
 // One run of an uploaded plan (contiguous cache, or a page pool when `pg`).
-int absorbed_run(const mla_absorbed_plan* p, const void* q, const void* kv, float sm_scale,
-                 void* out, float* lse, hipStream_t stream, const mla::PagedKv* pg) {
+// q_rows / kv_rows / num_heads: the sizes of the caller's tensors (kv_rows is
+// not checked for a page pool).
+int absorbed_run(const mla_absorbed_plan* p, const void* q, const void* kv, int64_t q_rows,
+                 int64_t kv_rows, int32_t num_heads, float sm_scale, void* out, float* lse,
+                 hipStream_t stream, const mla::PagedKv* pg) {
     if (p == nullptr) return fail(MLA_EINVAL, "plan is NULL");
     if (!p->planned) return fail(MLA_ESTATE, "plan has not been built");
-    if (!p->uploaded) return fail(MLA_ESTATE, "plan has not been uploaded");
     if (p->paged != (pg != nullptr)) return fail(MLA_ESTATE, "plan and call disagree on paged cache");
+    if (num_heads != p->num_heads) return fail(MLA_ESTATE, "num_heads differs from the plan");
+    if (q_rows != p->tq)
+        return fail(MLA_ESTATE, "q / out rows differ from the planned qo_indptr[batch]");
+    if (pg == nullptr && kv_rows < p->tk)
+        return fail(MLA_ESTATE, "kv has fewer rows than the planned kv_indptr[batch]");
+    if (!p->uploaded) return fail(MLA_ESTATE, "plan has not been uploaded");
     if (int s = check_scale(sm_scale)) return s;
     if (p->tq > 0 && (q == nullptr || out == nullptr))
         return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
@@ -451,7 +554,7 @@ int absorbed_run(const mla_absorbed_plan* p, const void* q, const void* kv, floa
         e = mla::launch_merge_splits(part_o, part_lse, p->splits, p->rows, out, lse, stream);
         if (e != hipSuccess) return hip_fail(e, "KV-split merge kernel launch");
     }
-    return MLA_OK;
+    return p->last_run.record(stream);
 }
 
 // One-shot absorbed call (plan + upload + run) with a plan kept per (device,
@@ -506,7 +609,7 @@ int absorbed_call(const void* q, const void* kv, const int32_t* qo_indptr,
     p->planned = true;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (int r = absorbed_upload(p, s)) return r;
-    return absorbed_run(p, q, kv, sm_scale, out, lse, s, pg);
+    return absorbed_run(p, q, kv, p->tq, p->tk, num_heads, sm_scale, out, lse, s, pg);
 }
 
 }  // namespace
@@ -553,15 +656,18 @@ int mla_ragged_plan(mla_plan* plan, const int32_t* qo_indptr, const int32_t* kv_
 int mla_plan_upload(mla_plan* plan, void* stream) {
     if (plan == nullptr) return fail(MLA_EINVAL, "plan is NULL");
     if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
-    int s = plan->dwl.upload(plan->items, static_cast<hipStream_t>(stream));
+    int s = plan->dwl.upload(plan->items, static_cast<hipStream_t>(stream),
+                             [plan] { plan->last_run.wait(); });
     if (s != MLA_OK) return s;
     plan->uploaded = true;
     return MLA_OK;
 }
 
 int mla_ragged_run(const mla_plan* plan, const void* q, const void* k, const void* v,
-                   float sm_scale, int32_t dtype, void* out, float* lse, void* stream) {
-    return do_run(plan, q, k, v, sm_scale, dtype, out, lse, static_cast<hipStream_t>(stream));
+                   int64_t q_rows, int64_t kv_rows, int32_t num_heads, float sm_scale,
+                   int32_t dtype, void* out, float* lse, void* stream) {
+    return do_run(plan, q, k, v, q_rows, kv_rows, num_heads, sm_scale, dtype, out, lse,
+                  static_cast<hipStream_t>(stream));
 }
 
 int mla_plan_info(const mla_plan* plan, int64_t* n_items, int32_t* block_m, int32_t* n_xcd,
@@ -760,15 +866,17 @@ int mla_absorbed_plan_upload(mla_absorbed_plan* plan, void* stream) {
     return absorbed_upload(plan, static_cast<hipStream_t>(stream));
 }
 
-int mla_absorbed_run(const mla_absorbed_plan* plan, const void* q, const void* kv, float sm_scale,
+int mla_absorbed_run(const mla_absorbed_plan* plan, const void* q, const void* kv,
+                     int64_t q_rows, int64_t kv_rows, int32_t num_heads, float sm_scale,
                      void* out, float* lse, void* stream) {
-    return absorbed_run(plan, q, kv, sm_scale, out, lse, static_cast<hipStream_t>(stream), nullptr);
+    return absorbed_run(plan, q, kv, q_rows, kv_rows, num_heads, sm_scale, out, lse,
+                        static_cast<hipStream_t>(stream), nullptr);
 }
 
 int mla_absorbed_run_paged(const mla_absorbed_plan* plan, const void* q, const void* kv_cache,
-                           const int32_t* block_table, int32_t max_pages, int32_t page_size,
-                           int32_t num_pages, float sm_scale, void* out, float* lse,
-                           void* stream) {
+                           int64_t q_rows, int32_t num_heads, const int32_t* block_table,
+                           int32_t max_pages, int32_t page_size, int32_t num_pages,
+                           float sm_scale, void* out, float* lse, void* stream) {
     if (page_size < 32 || page_size % 32 != 0)
         return fail(MLA_EINVAL, "page_size must be a positive multiple of 32");
     if (max_pages < 1 || num_pages < 1) return fail(MLA_EINVAL, "max_pages and num_pages must be >= 1");
@@ -776,8 +884,8 @@ int mla_absorbed_run_paged(const mla_absorbed_plan* plan, const void* q, const v
         (block_table == nullptr || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))
         return fail(MLA_EINVAL, "block_table must be non-NULL and 4-byte aligned");
     const mla::PagedKv pg{block_table, max_pages, page_size, num_pages};
-    return absorbed_run(plan, q, kv_cache, sm_scale, out, lse, static_cast<hipStream_t>(stream),
-                        &pg);
+    return absorbed_run(plan, q, kv_cache, q_rows, -1, num_heads, sm_scale, out, lse,
+                        static_cast<hipStream_t>(stream), &pg);
 }
 
 int mla_absorbed_plan_info(const mla_absorbed_plan* plan, int64_t* n_items, int32_t* splits) {

@@ -75,11 +75,14 @@ __device__ __forceinline__ void merge_row_chunk(const u32x4_t xa, const u32x4_t 
     }
 }
 
+// No pointer is declared __restrict__: o may alias o_a or o_b and lse may
+// alias lse_a or lse_b (an in-place merge). Each output chunk depends only on
+// the same row's inputs, loaded by the same lane (the LSE by every lane of
+// the row's wave) before that lane stores.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void merge_kernel(
-    const void* __restrict__ o_a, const float* __restrict__ lse_a, const void* __restrict__ o_b,
-    const float* __restrict__ lse_b, void* __restrict__ o, float* __restrict__ lse,
-    int64_t num_rows) {
+    const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
+    float* lse, int64_t num_rows) {
     constexpr int kLanesPerRow = kBf16 ? kDvo * 2 / 16 : kDvo * 4 / 16;
     constexpr int kUnroll = 2;      // two rows' chunks in flight per lane
     const int64_t total = num_rows * kLanesPerRow;

@@ -106,8 +106,13 @@ int main() {
                                                   trial % 2) == MLA_OK;
                 int32_t splits = 0;
                 checks += mla_absorbed_plan_info(ap, &n, &splits) == MLA_OK;
-                checks += mla_absorbed_run(ap, nullptr, nullptr, 0.1f, nullptr, nullptr,
-                                           nullptr) == MLA_ESTATE;   // not uploaded
+                // not uploaded (or built for a page pool): a state error
+                checks += mla_absorbed_run(ap, nullptr, nullptr, batch > 0 ? qo[batch] : 0,
+                                           batch > 0 ? kv[batch] : 0, heads, 0.1f, nullptr,
+                                           nullptr, nullptr) == MLA_ESTATE;
+                // sizes that do not match the plan: a state error too
+                checks += mla_absorbed_run(ap, nullptr, nullptr, -1, 0, heads, 0.1f, nullptr,
+                                           nullptr, nullptr) == MLA_ESTATE;
                 mla_absorbed_plan_destroy(ap);
             }
         }

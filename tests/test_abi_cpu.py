@@ -99,9 +99,29 @@ def test_merge_and_decompress_reject_invalid_arguments():
 def test_run_before_upload_is_a_state_error():
     p = mra.Plan()
     lib = mra.lib()
-    assert lib.mla_ragged_run(p._h, 16, 16, 16, 0.1, 0, 16, 16, None) == 5
+    assert lib.mla_ragged_run(p._h, 16, 16, 16, 4, 4, 2, 0.1, 0, 16, 16, None) == 5
     p.plan([0, 4], [0, 4], 2, True)
-    assert lib.mla_ragged_run(p._h, 16, 16, 16, 0.1, 0, 16, 16, None) == 5   # not uploaded
+    assert lib.mla_ragged_run(p._h, 16, 16, 16, 4, 4, 2, 0.1, 0, 16, 16, None) == 5   # not uploaded
+    assert b"uploaded" in lib.mla_last_error()
+
+
+@pytest.mark.parametrize("q_rows,kv_rows,heads,dtype,what", [
+    (5, 9, 2, 0, b"q / out rows"),        # q rows differ from qo_indptr[batch]
+    (3, 9, 2, 0, b"q / out rows"),
+    (4, 8, 2, 0, b"fewer rows"),          # k / v shorter than kv_indptr[batch]
+    (4, 9, 3, 0, b"num_heads"),           # other head count
+    (4, 9, 2, 1, b"dtype"),               # other dtype
+])
+def test_run_rejects_tensors_that_do_not_match_the_plan(q_rows, kv_rows, heads, dtype, what):
+    # checked before the upload state, so this runs without a GPU
+    p = mra.Plan().plan([0, 1, 4], [0, 3, 9], 2, True)
+    lib = mra.lib()
+    assert lib.mla_ragged_run(p._h, 16, 16, 16, q_rows, kv_rows, heads, 0.1, dtype, 16, 16,
+                              None) == 5
+    assert what in lib.mla_last_error()
+    # sizes that match (k / v may be longer) reach the upload check
+    assert lib.mla_ragged_run(p._h, 16, 16, 16, 4, 12, 2, 0.1, 0, 16, 16, None) == 5
+    assert b"uploaded" in lib.mla_last_error()
 
 
 # ---------------------------------------------------------------------------
@@ -438,7 +458,7 @@ def test_absorbed_plan_states_and_info_without_a_gpu():
     lib = mra.lib()
     p = mra.AbsorbedPlan()
     # not built: every run is a state error, before any HIP call
-    assert lib.mla_absorbed_run(p._h, 16, 16, 0.1, 16, 16, None) == 5
+    assert lib.mla_absorbed_run(p._h, 16, 16, 2, 8192, 128, 0.1, 16, 16, None) == 5
     assert lib.mla_absorbed_plan_info(p._h, None, None) == 5
     qo = np.array([0, 1, 2], dtype=np.int32)
     kv = np.array([0, 4096, 8192], dtype=np.int32)
@@ -446,13 +466,21 @@ def test_absorbed_plan_states_and_info_without_a_gpu():
     info = p.info()
     assert info["kv_splits"] > 1 and info["n_items"] % 8 == 0
     # built, not uploaded
-    assert lib.mla_absorbed_run(p._h, 16, 16, 0.1, 16, 16, None) == 5
+    assert lib.mla_absorbed_run(p._h, 16, 16, 2, 8192, 128, 0.1, 16, 16, None) == 5
+    assert b"uploaded" in lib.mla_last_error()
+    # tensors that do not match the plan: state errors, before the upload check
+    for q_rows, kv_rows, heads, what in ((3, 8192, 128, b"q / out rows"),
+                                         (2, 8191, 128, b"fewer rows"),
+                                         (2, 8192, 64, b"num_heads")):
+        assert lib.mla_absorbed_run(p._h, 16, 16, q_rows, kv_rows, heads, 0.1, 16, 16,
+                                    None) == 5
+        assert what in lib.mla_last_error()
     # built for a contiguous cache: a paged run is a state error
     bt = np.zeros(4, dtype=np.int32)
-    assert lib.mla_absorbed_run_paged(p._h, 16, 16, bt.ctypes.data, 128, 32, 256, 0.1, 16, 16,
-                                      None) == 5
-    assert lib.mla_absorbed_run_paged(p._h, 16, 16, bt.ctypes.data, 128, 48, 256, 0.1, 16, 16,
-                                      None) == 1          # page size
+    assert lib.mla_absorbed_run_paged(p._h, 16, 16, 2, 128, bt.ctypes.data, 128, 32, 256, 0.1,
+                                      16, 16, None) == 5
+    assert lib.mla_absorbed_run_paged(p._h, 16, 16, 2, 128, bt.ctypes.data, 128, 48, 256, 0.1,
+                                      16, 16, None) == 1          # page size
     with pytest.raises(RuntimeError):
         p.plan([0, 3, 2], [0, 1, 2], 4, True)              # decreasing indptr
     assert lib.mla_absorbed_plan_build(p._h, qo.ctypes.data, kv.ctypes.data, 2, 4, 1, 2) == 1
@@ -481,3 +509,10 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         mra.absorbed_prefill(torch.zeros((t, h, 576), dtype=torch.bfloat16),
                              torch.zeros((t, 576), dtype=torch.bfloat16), ind, ind, True, 0.1)
+
+
+def test_binding_block_m_matches_the_planner():
+    # the full-size GPU tests sample rows on both sides of every query-tile
+    # edge using the binding's constant
+    p = mra.Plan().plan([0, 300], [0, 300], 2, True)
+    assert p.info()["block_m"] == mra.PREFILL_BLOCK_M

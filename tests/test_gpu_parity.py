@@ -523,8 +523,9 @@ def test_deepseek_v3_batch_full_size():
     o, lse = mra.ragged_prefill(g.q, g.k, g.v, g.qo_indptr, g.kv_indptr, True, g.sm_scale)
     torch.cuda.synchronize()
     _row_properties(o, lse)
-    rows = sample_rows(g.qo_indptr, n_random=128, seed=2)
-    _sampled_parity(g, o, lse, [0, 77, 127], rows, "deepseek_v3_batch")
+    # both sides of every 128-row query-tile edge, sequence ends, random rows
+    rows = sample_rows(g.qo_indptr, block=mra.PREFILL_BLOCK_M, n_random=128, seed=2)
+    _sampled_parity(g, o, lse, [0, 41, 77, 127], rows, "deepseek_v3_batch")
 
 
 def test_chunked_prefill_full_size():
@@ -539,9 +540,9 @@ def test_chunked_prefill_full_size():
         o, lse = mra.merge_state(o, lse, o2, l2)
     torch.cuda.synchronize()
     _row_properties(o, lse)
-    rows = sample_rows(m.qo_indptr, n_random=64, seed=3)
+    rows = sample_rows(m.qo_indptr, block=mra.PREFILL_BLOCK_M, n_random=64, seed=3)
     idx = torch.tensor(rows)
-    for h in (0, 101):
+    for h in (0, 57, 101, 127):
         q = head_slice(m.q, h)
         chunk_kvs = [(head_slice(ch.k, h), head_slice(ch.v, h), ch.kv_indptr) for ch in c.chunks]
         ro, rl, rparts = oracle.chunked(q, head_slice(m.k, h), head_slice(m.v, h), m.qo_indptr,
@@ -560,9 +561,11 @@ def test_skewed_batch_full_size():
     o, lse = mra.ragged_prefill(g.q, g.k, g.v, g.qo_indptr, g.kv_indptr, True, g.sm_scale)
     torch.cuda.synchronize()
     _row_properties(o, lse)
-    rows = sample_rows(g.qo_indptr, n_random=64, seed=4)
-    rows = rows[::3]   # keep the oracle to seconds
-    _sampled_parity(g, o, lse, [5], rows, "skewed_batch")
+    # every tile-edge row (both sides of each 128-row edge) and both ends of
+    # every sequence, including the longest ones, plus random rows
+    rows = sample_rows(g.qo_indptr, block=mra.PREFILL_BLOCK_M, n_random=64, seed=4)
+    _flush(f"[gpu] skewed_batch: {len(rows)} sampled rows x 4 heads against the oracle")
+    _sampled_parity(g, o, lse, [0, 5, 64, 127], rows, "skewed_batch")
     del g, o, lse
     torch.cuda.empty_cache()
 
@@ -576,9 +579,9 @@ def test_decompress_then_prefill_full_size():
     torch.cuda.synchronize()
     _row_properties(o, lse)
     c_kv, k_rope = d.c_kv.cpu(), d.k_rope.cpu()
-    rows = sample_rows(d.indptr, n_random=32, seed=5)
+    rows = sample_rows(d.indptr, block=mra.PREFILL_BLOCK_M, n_random=32, seed=5)
     idx = torch.tensor(rows)
-    for h in (3, H - 2):
+    for h in (0, 3, H - 2, H - 1):
         wk = d.w_uk[:, h * 128:(h + 1) * 128].contiguous().cpu()
         wv = d.w_uv[:, h * 128:(h + 1) * 128].contiguous().cpu()
         rk, rv = oracle.decompress(c_kv, k_rope, wk, wv, 1)           # fp64, all tokens
@@ -591,6 +594,129 @@ def test_decompress_then_prefill_full_size():
         ro, rl = oracle.prefill(qh, rk, rv, d.indptr, d.indptr, True, d.sm_scale, rows)
         check(o[idx, h:h + 1].cpu(), lse[idx, h:h + 1].cpu(), ro, rl, torch.bfloat16,
               f"decompress+prefill head {h}")
+
+
+def _paged_cache_on_gpu(k, v, kv_indptr, page, seed):
+    """Page pools [P, page, H, D] holding the contiguous K/V of every sequence
+    in a seeded random page order (plus two pages of zeros), built on the GPU,
+    and the block table [batch, max_pages]."""
+    lens = [b - a for a, b in zip(kv_indptr, kv_indptr[1:])]
+    per = [-(-n // page) for n in lens]
+    total = sum(per) + 2
+    perm = torch.randperm(total, generator=torch.Generator().manual_seed(seed)).tolist()
+    h = k.shape[1]
+    kc = torch.zeros((total, page, h, k.shape[2]), dtype=k.dtype, device=k.device)
+    vc = torch.zeros((total, page, h, v.shape[2]), dtype=v.dtype, device=v.device)
+    table = torch.full((len(lens), max(max(per), 1)), -1, dtype=torch.int32)
+    i = 0
+    for b, n in enumerate(lens):
+        for pg in range(per[b]):
+            phys = perm[i]
+            i += 1
+            table[b, pg] = phys
+            a = kv_indptr[b] + pg * page
+            m = min(page, n - pg * page)
+            kc[phys, :m] = k[a:a + m]
+            vc[phys, :m] = v[a:a + m]
+    return kc, vc, table.to(k.device)
+
+
+def test_full_size_entry_points_are_bit_identical():
+    """The DeepSeek-V3-shaped batch (16 sequences, 128 heads) through the
+    device-planned call (eager, then replayed twice from a captured graph
+    with eager work and synchronisation between the replays), a plan with
+    2-head items, and the paged call (64-key pages in random order): every
+    output equals the one-shot call's bit for bit."""
+    g = workloads.deepseek_v3_batch(device=DEV)
+    t = g.qo_indptr[-1]
+    _flush(f"[gpu] full-size entry points: T={t} H={g.num_heads}")
+    ref_o, ref_l = mra.ragged_prefill(g.q, g.k, g.v, g.qo_indptr, g.kv_indptr, True, g.sm_scale)
+    torch.cuda.synchronize()
+    qo_d = torch.tensor(g.qo_indptr, dtype=torch.int32, device=DEV)
+    dp = mra.DevicePlan(len(g.qo_indptr) - 1, t, t, g.num_heads)
+    o, l = dp.run(g.q, g.k, g.v, qo_d, qo_d, True, g.sm_scale)
+    torch.cuda.synchronize()
+    assert int(dp.invalid_flag().item()) == 0
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l), "device plan (eager)"
+    _flush("[gpu] full-size device plan: graph capture and replays")
+    out = torch.zeros_like(ref_o)
+    lse = torch.zeros_like(ref_l)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dp.run(g.q, g.k, g.v, qo_d, qo_d, True, g.sm_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"graph replay {rep}"
+        # eager work between the replays
+        o2, l2 = mra.ragged_prefill(g.q, g.k, g.v, g.qo_indptr, g.kv_indptr, True, g.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, ref_o) and torch.equal(l2, ref_l), "one-shot between replays"
+    del graph, out, lse, o2, l2
+    p = mra.Plan(heads_per_item=2).plan(g.qo_indptr, g.kv_indptr, g.num_heads, True).upload()
+    o, l = p.run(g.q, g.k, g.v, g.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l), "plan with 2-head items"
+    del p, o, l
+    _flush("[gpu] full-size paged call (64-key pages)")
+    kc, vc, table = _paged_cache_on_gpu(g.k, g.v, g.kv_indptr, 64, seed=70)
+    o, l = mra.ragged_prefill_paged(g.q, kc, vc, g.qo_indptr, g.kv_indptr, table, True,
+                                    g.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l), "paged"
+    del kc, vc, table, o, l, g
+    torch.cuda.empty_cache()
+
+
+def test_plan_run_rejects_tensors_that_do_not_match_the_plan():
+    x = _to(workloads.ragged_inputs([40, 90], [50, 90], 4, torch.bfloat16, seed=71), DEV)
+    p = mra.Plan().plan(x.qo_indptr, x.kv_indptr, 4, True).upload()
+    o, l = p.run(x.q, x.k, x.v, x.sm_scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = mra.ragged_prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    for q, k, v in ((x.q[:-1], x.k, x.v),                  # fewer query rows than planned
+                    (x.q, x.k[:-1], x.v[:-1]),             # fewer key rows than planned
+                    (x.q[:, :2], x.k[:, :2], x.v[:, :2])):  # other head count
+        with pytest.raises(mra.MlaError) as e:
+            p.run(q.contiguous(), k.contiguous(), v.contiguous(), x.sm_scale)
+        assert e.value.status == 5
+    torch.cuda.synchronize()
+
+
+def test_growing_one_shot_does_not_wait_for_other_streams():
+    """A one-shot call whose work list outgrows its stream's buffer returns
+    while a long kernel on another stream is still running (no device-wide
+    synchronisation), and its result is still exact."""
+    small = _to(workloads.ragged_inputs([64], [64], 2, torch.bfloat16, seed=72), DEV)
+    lens = [700, 300, 1000, 513]
+    big = _to(workloads.ragged_inputs(lens, lens, 8, torch.bfloat16, seed=73), DEV)
+    ref_o, ref_l = mra.ragged_prefill(big.q, big.k, big.v, big.qo_indptr, big.kv_indptr, True,
+                                      big.sm_scale)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(sa):          # this stream's plan starts with a one-item list
+        mra.ragged_prefill(small.q, small.k, small.v, small.qo_indptr, small.kv_indptr, True,
+                           small.sm_scale)
+    torch.cuda.synchronize()
+    _flush("[gpu] spin kernel on stream B, growing one-shot call on stream A")
+    done_b = torch.cuda.Event()
+    with torch.cuda.stream(sb):
+        torch.cuda._sleep(2_000_000_000)    # about a second of clock cycles
+        done_b.record(sb)
+    with torch.cuda.stream(sa):
+        o, l = mra.ragged_prefill(big.q, big.k, big.v, big.qo_indptr, big.kv_indptr, True,
+                                  big.sm_scale)
+    still_running = not done_b.query()
+    sa.synchronize()
+    torch.cuda.synchronize()
+    assert still_running, "the growing call waited for the other stream's kernel"
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
 
 
 # ---------------------------------------------------------------------------
