@@ -476,9 +476,13 @@ def test_merge_state_in_place():
 # decompression
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("num_seqs,seq_len,num_heads", [(2, 300, 3), (1, 17, 1), (3, 129, 4)])
+@pytest.mark.parametrize("num_seqs,seq_len,num_heads", [
+    (2, 300, 3), (1, 17, 1), (3, 129, 4),
+    (1, 4113, 16),   # many 32-token tiles per workgroup, a ragged last tile, empty token ranges
+    (1, 33, 128),    # 128 heads, two tiles (the second holds one token)
+    (2, 500, 5)])
 def test_decompress_small_parity(num_seqs, seq_len, num_heads):
-    # ragged token tails (not multiples of the 256-token tile), odd head counts
+    # ragged token tails (not multiples of the 32-token tile), odd head counts
     d = workloads.decompress_batch(num_seqs=num_seqs, seq_len=seq_len, num_heads=num_heads)
     _flush(f"[gpu] decompress T={num_seqs * seq_len} H={num_heads}")
     k, v = mra.decompress_kv(d.c_kv.to(DEV), d.k_rope.to(DEV), d.w_uk.to(DEV), d.w_uv.to(DEV),
