@@ -263,6 +263,33 @@ int mla_ragged_prefill_device_plan(const void *q, const void *k, const void *v,
                                    int64_t workspace_bytes, void *stream);
 
 /*
+ * Allocation-free form of mla_ragged_prefill_device_plan, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same operation, arguments and
+ * outputs, but the device-plan workspace is a 16 MiB array inside the
+ * library (a file-scope __device__ array; each GPU the library runs on holds
+ * its own copy until the process ends), so the call allocates nothing, makes
+ * no synchronising call and takes no workspace argument.
+ *   Limit: the batch's workspace (see mla_device_plan_workspace_size) must
+ *   fit in MLA_NOALLOC_SCRATCH_BYTES, e.g. 128 heads over 262,144 query
+ *   tokens in 64 sequences needs 7.9 MB; larger calls return
+ *   MLA_EUNSUPPORTED before any HIP call.
+ *   Sharing: every call on one GPU uses that GPU's array. Calls that can
+ *   overlap on one GPU (concurrent streams, or threads without ordering)
+ *   race on it and must be serialised by the caller, e.g. issued on one
+ *   stream. Each call rewrites every word it reads, so no clearing is needed
+ *   between calls. Sequences with invalid device indptrs are skipped as in
+ *   the workspace form; this form does not report the flag word.
+ * Outputs are identical bit for bit to mla_ragged_prefill_device_plan's.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (16 << 20)
+int mla_ragged_prefill_device_plan_noalloc(const void *q, const void *k, const void *v,
+                                           const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                           int32_t batch, int64_t max_tq, int64_t max_tk,
+                                           int32_t num_heads, int32_t causal, float sm_scale,
+                                           int32_t dtype, void *out, float *lse, void *stream);
+
+/*
  * merge_state: combine two attention states computed over disjoint key sets
  * (the chunked-prefill combine of the causal new-token pass with the
  * non-causal context-chunk passes; the pages return each pass's (O, LSE)

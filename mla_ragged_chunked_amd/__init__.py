@@ -22,7 +22,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-__all__ = ["ragged_prefill", "ragged_prefill_paged", "merge_state", "decompress_kv",
+__all__ = ["ragged_prefill", "ragged_prefill_paged", "ragged_prefill_device_plan_noalloc",
+           "merge_state", "decompress_kv",
            "absorbed_prefill", "absorbed_prefill_paged", "absorbed_plan_items", "AbsorbedPlan", "Plan", "DevicePlan", "MlaError", "lib",
            "LIB_PATH", "DQK", "DVO", "DLAT", "DROPE", "PREFILL_BLOCK_M", "EXPORTED_SYMBOLS"]
 
@@ -38,7 +39,8 @@ EXPORTED_SYMBOLS = [
     "mla_plan_create", "mla_plan_destroy", "mla_ragged_plan", "mla_plan_upload",
     "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_set_xcds",
     "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
-    "mla_ragged_prefill_device_plan", "mla_ragged_prefill_paged",
+    "mla_ragged_prefill_device_plan", "mla_ragged_prefill_device_plan_noalloc",
+    "mla_ragged_prefill_paged",
     "mla_merge_state", "mla_decompress_kv", "mla_absorbed_prefill", "mla_absorbed_plan_items",
     "mla_absorbed_prefill_paged", "mla_absorbed_plan_create", "mla_absorbed_plan_destroy",
     "mla_absorbed_plan_build", "mla_absorbed_plan_upload", "mla_absorbed_run",
@@ -87,6 +89,8 @@ def lib():
         "mla_device_plan_workspace_size": ([I32, I64, I32, I32, ctypes.POINTER(I64)], ctypes.c_int),
         "mla_ragged_prefill_device_plan": ([P, P, P, P, P, I32, I64, I64, I32, I32, F, I32, P, P,
                                             P, I64, P], ctypes.c_int),
+        "mla_ragged_prefill_device_plan_noalloc": ([P, P, P, P, P, I32, I64, I64, I32, I32, F,
+                                                    I32, P, P, P], ctypes.c_int),
         "mla_ragged_prefill_paged": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, I32, P,
                                       P, P], ctypes.c_int),
         "mla_merge_state": ([P, P, P, P, P, P, I64, I32, I32, P], ctypes.c_int),
@@ -265,6 +269,35 @@ class DevicePlan:
                 self.workspace.data_ptr(), self.workspace.numel(), _stream(q.device)),
                 "mla_ragged_prefill_device_plan")
         return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def ragged_prefill_device_plan_noalloc(q, k, v, qo_indptr: torch.Tensor,
+                                       kv_indptr: torch.Tensor, max_tq: int, max_tk: int,
+                                       causal: bool, sm_scale: float, out: torch.Tensor,
+                                       lse: Optional[torch.Tensor] = None):
+    """Device-planned prefill with the library's static scratch as workspace:
+    allocates nothing (out, and lse if wanted, are the caller's). Device int32
+    indptrs of length batch + 1; q/out hold at least max_tq rows, k/v max_tk.
+    Calls that can overlap on one GPU share the scratch and must be ordered."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (qo_indptr, "qo_indptr"),
+                    (kv_indptr, "kv_indptr"), (out, "out")):
+        _dev_tensor(t, name)
+    if qo_indptr.dtype != torch.int32 or kv_indptr.dtype != torch.int32 or \
+            qo_indptr.numel() != kv_indptr.numel() or qo_indptr.numel() < 1:
+        raise ValueError("device indptrs must be int32 with batch + 1 entries each")
+    if q.shape[0] < max_tq or k.shape[0] < max_tk:
+        raise ValueError("q must hold max_tq rows and k, v max_tk rows")
+    _check_shapes(q, k, v, out, lse)
+    with torch.cuda.device(q.device):
+        _check(lib().mla_ragged_prefill_device_plan_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(qo_indptr), _ptr(kv_indptr), qo_indptr.numel() - 1,
+            int(max_tq), int(max_tk), q.shape[1], int(bool(causal)), float(sm_scale),
+            _DT[q.dtype], _ptr(out), _ptr(lse), _stream(q.device)),
+            "mla_ragged_prefill_device_plan_noalloc")
+    return (out, lse) if lse is not None else out
 
 
 def _check_shapes(q, k, v, out, lse):

@@ -612,6 +612,59 @@ int absorbed_call(const void* q, const void* kv, const int32_t* qo_indptr,
     return absorbed_run(p, q, kv, p->tq, p->tk, num_heads, sm_scale, out, lse, s, pg);
 }
 
+// Device-planned prefill: the caller's workspace, or (use_scratch) the
+// library's file-scope scratch array. Validates everything on the host
+// before the first HIP call; allocates nothing and makes no synchronising
+// call, so it can be captured in a graph.
+int device_plan_call(const void* q, const void* k, const void* v, const int32_t* qo_indptr,
+                     const int32_t* kv_indptr, int32_t batch, int64_t max_tq, int64_t max_tk,
+                     int32_t num_heads, int32_t causal, float sm_scale, int32_t dtype, void* out,
+                     float* lse, void* workspace, int64_t workspace_bytes, bool use_scratch,
+                     void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_scale(sm_scale)) return s;
+    if (batch < 0 || batch > mla::kDevicePlanMaxBatch)
+        return fail(MLA_EINVAL, "batch must be in [0, 4096] for device planning");
+    if (num_heads < 1 || num_heads > 65535) return fail(MLA_EINVAL, "num_heads must be in [1, 65535]");
+    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
+    if (max_tq < 0 || max_tk < 0) return fail(MLA_EINVAL, "max_tq and max_tk must be >= 0");
+    if (max_tq * num_heads > INT32_MAX || max_tk * num_heads > INT32_MAX)
+        return fail(MLA_EUNSUPPORTED, "tokens x heads exceeds 2^31 rows");
+    if (batch == 0) return MLA_OK;
+    if (qo_indptr == nullptr || kv_indptr == nullptr) return fail(MLA_EINVAL, "indptr is NULL");
+    if (int s = check_tensors(q, k, v, out, lse, max_tq, max_tk)) return s;
+    const int bm = dtype == MLA_DTYPE_BF16 ? mla::prefill_bf16_block_m() : mla::prefill_fp32_block_m();
+    const int64_t n = mla::device_plan_max_items(batch, max_tq, num_heads, bm);
+    const mla::DevicePlanLayout l = mla::device_plan_layout(batch, n);
+    if (n > INT32_MAX) return fail(MLA_EUNSUPPORTED, "too many work items");
+    if (use_scratch) {
+        if (l.bytes > mla::kDevicePlanScratchBytes)
+            return fail(MLA_EUNSUPPORTED,
+                        "this batch needs " + std::to_string(l.bytes) +
+                            " bytes of device-plan workspace; the static scratch holds " +
+                            std::to_string(mla::kDevicePlanScratchBytes) +
+                            " (use mla_ragged_prefill_device_plan with a workspace)");
+        hipError_t e = mla::device_plan_scratch(&workspace);
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+    } else {
+        if (workspace == nullptr || !aligned16(workspace))
+            return fail(MLA_EINVAL, "workspace must be non-NULL and 16-byte aligned");
+        if (workspace_bytes < l.bytes)
+            return fail(MLA_EINVAL, "workspace is smaller than mla_device_plan_workspace_size");
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = mla::launch_device_plan(qo_indptr, kv_indptr, batch, max_tq, max_tk, num_heads,
+                                           causal != 0, bm, workspace, n, s);
+    if (e != hipSuccess) return hip_fail(e, "device plan launch");
+    const WorkItem* items =
+        reinterpret_cast<const WorkItem*>(static_cast<const uint8_t*>(workspace) + l.items);
+    e = dtype == MLA_DTYPE_BF16
+            ? mla::launch_prefill_bf16(items, n, q, k, v, out, lse, num_heads, sm_scale, s)
+            : mla::launch_prefill_fp32(items, n, q, k, v, out, lse, num_heads, sm_scale, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -757,39 +810,18 @@ int mla_ragged_prefill_device_plan(const void* q, const void* k, const void* v,
                                    int32_t num_heads, int32_t causal, float sm_scale,
                                    int32_t dtype, void* out, float* lse, void* workspace,
                                    int64_t workspace_bytes, void* stream) {
-    // validate everything before the first HIP call (the indptrs stay on the
-    // device and are checked there)
-    if (int s = check_dtype(dtype)) return s;
-    if (int s = check_scale(sm_scale)) return s;
-    if (batch < 0 || batch > mla::kDevicePlanMaxBatch)
-        return fail(MLA_EINVAL, "batch must be in [0, 4096] for device planning");
-    if (num_heads < 1 || num_heads > 65535) return fail(MLA_EINVAL, "num_heads must be in [1, 65535]");
-    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
-    if (max_tq < 0 || max_tk < 0) return fail(MLA_EINVAL, "max_tq and max_tk must be >= 0");
-    if (max_tq * num_heads > INT32_MAX || max_tk * num_heads > INT32_MAX)
-        return fail(MLA_EUNSUPPORTED, "tokens x heads exceeds 2^31 rows");
-    if (batch == 0) return MLA_OK;
-    if (qo_indptr == nullptr || kv_indptr == nullptr) return fail(MLA_EINVAL, "indptr is NULL");
-    if (int s = check_tensors(q, k, v, out, lse, max_tq, max_tk)) return s;
-    if (workspace == nullptr || !aligned16(workspace))
-        return fail(MLA_EINVAL, "workspace must be non-NULL and 16-byte aligned");
-    const int bm = dtype == MLA_DTYPE_BF16 ? mla::prefill_bf16_block_m() : mla::prefill_fp32_block_m();
-    const int64_t n = mla::device_plan_max_items(batch, max_tq, num_heads, bm);
-    const mla::DevicePlanLayout l = mla::device_plan_layout(batch, n);
-    if (workspace_bytes < l.bytes)
-        return fail(MLA_EINVAL, "workspace is smaller than mla_device_plan_workspace_size");
-    if (n > INT32_MAX) return fail(MLA_EUNSUPPORTED, "too many work items");
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = mla::launch_device_plan(qo_indptr, kv_indptr, batch, max_tq, max_tk, num_heads,
-                                           causal != 0, bm, workspace, n, s);
-    if (e != hipSuccess) return hip_fail(e, "device plan launch");
-    const WorkItem* items =
-        reinterpret_cast<const WorkItem*>(static_cast<const uint8_t*>(workspace) + l.items);
-    e = dtype == MLA_DTYPE_BF16
-            ? mla::launch_prefill_bf16(items, n, q, k, v, out, lse, num_heads, sm_scale, s)
-            : mla::launch_prefill_fp32(items, n, q, k, v, out, lse, num_heads, sm_scale, s);
-    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
-    return MLA_OK;
+    return device_plan_call(q, k, v, qo_indptr, kv_indptr, batch, max_tq, max_tk, num_heads,
+                            causal, sm_scale, dtype, out, lse, workspace, workspace_bytes, false,
+                            stream);
+}
+
+int mla_ragged_prefill_device_plan_noalloc(const void* q, const void* k, const void* v,
+                                           const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                           int32_t batch, int64_t max_tq, int64_t max_tk,
+                                           int32_t num_heads, int32_t causal, float sm_scale,
+                                           int32_t dtype, void* out, float* lse, void* stream) {
+    return device_plan_call(q, k, v, qo_indptr, kv_indptr, batch, max_tq, max_tk, num_heads,
+                            causal, sm_scale, dtype, out, lse, nullptr, 0, true, stream);
 }
 
 int mla_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,

@@ -22,9 +22,20 @@
 // Invalid device indptrs (decreasing, negative, or beyond max_tq / max_tk)
 // turn the offending sequence into no work, and set a flag word in the
 // workspace, so a bad input can neither fault nor read out of bounds.
+#include <map>
+#include <mutex>
+
 #include "internal.h"
 
 namespace mla {
+
+// Workspace of the allocation-free entry point: a file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// In host code `scratch` is only a stand-in for the symbol, never a device
+// address: device_plan_scratch() resolves the array's address on the
+// current device and every kernel argument uses that address.
+__device__ __align__(256) uint8_t scratch[kDevicePlanScratchBytes];
+
 namespace {
 
 constexpr int kSortThreads = 1024;
@@ -182,6 +193,26 @@ DevicePlanLayout device_plan_layout(int batch, int64_t max_items) {
     l.items = l.prefix + up((int64_t)(batch + 1) * 4);
     l.bytes = l.items + max_items * (int64_t)sizeof(WorkItem);
     return l;
+}
+
+hipError_t device_plan_scratch(void** ptr) {
+    // resolved once per device, with that device current
+    static std::mutex mu;
+    static std::map<int, void*> addr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = addr.find(dev);
+    if (it == addr.end()) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        it = addr.emplace(dev, p).first;
+    }
+    *ptr = it->second;
+    return hipSuccess;
 }
 
 hipError_t launch_device_plan(const int32_t* qo, const int32_t* kv, int batch, int64_t max_tq,

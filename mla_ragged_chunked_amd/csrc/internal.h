@@ -105,6 +105,13 @@ constexpr int kDevicePlanXcds = 8;
 struct DevicePlanLayout {
     int64_t flag, order, prefix, items, bytes;
 };
+// Size of the device-plan workspace held in a file-scope device array for
+// the allocation-free entry point (it fits, e.g., 128 heads over 262,144
+// query tokens in 64 sequences: 7.9 MB of work list).
+constexpr int64_t kDevicePlanScratchBytes = INT64_C(16) << 20;
+// Device address of that array on the current device (resolved with
+// hipGetSymbolAddress on the first call per device).
+hipError_t device_plan_scratch(void** ptr);
 int64_t device_plan_max_items(int batch, int64_t max_tq, int num_heads, int block_m);
 DevicePlanLayout device_plan_layout(int batch, int64_t max_items);
 hipError_t launch_device_plan(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,

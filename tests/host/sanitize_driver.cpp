@@ -54,6 +54,7 @@ hipError_t launch_device_plan(const int32_t*, const int32_t*, int, int64_t, int6
                               int, void*, int64_t, hipStream_t) {
     return hipErrorInvalidValue;
 }
+hipError_t device_plan_scratch(void**) { return hipErrorInvalidValue; }
 }  // namespace mla
 
 int main() {
@@ -134,6 +135,16 @@ int main() {
                                    nullptr, nullptr, nullptr) != MLA_OK;
     checks += mla_merge_state(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 10, 128,
                               MLA_DTYPE_BF16, nullptr) != MLA_OK;
+    // the allocation-free device plan: oversize and invalid calls fail on the host
+    static int32_t dummy[64];
+    checks += mla_ragged_prefill_device_plan_noalloc(dummy, dummy, dummy, ok_kv.data(),
+                                                     ok_kv.data(), 2, 1000000, 1000000, 128, 1,
+                                                     0.1f, MLA_DTYPE_BF16, dummy, nullptr,
+                                                     nullptr) == MLA_EUNSUPPORTED;
+    checks += mla_ragged_prefill_device_plan_noalloc(dummy, dummy, dummy, ok_kv.data(),
+                                                     ok_kv.data(), 2, 8, 8, 0, 1, 0.1f,
+                                                     MLA_DTYPE_BF16, dummy, nullptr,
+                                                     nullptr) == MLA_EINVAL;
     std::printf("sanitize driver: %d checks passed\n", checks);
     return 0;
 }

@@ -516,3 +516,27 @@ def test_binding_block_m_matches_the_planner():
     # edge using the binding's constant
     p = mra.Plan().plan([0, 300], [0, 300], 2, True)
     assert p.info()["block_m"] == mra.PREFILL_BLOCK_M
+
+
+def test_noalloc_prefill_rejects_bad_calls_before_any_hip_call():
+    lib = mra.lib()
+    qo = np.array([0, 10], dtype=np.int32)
+    f = lib.mla_ragged_prefill_device_plan_noalloc
+    # a batch whose device-plan workspace exceeds the 16 MiB scratch array
+    # (128 heads, 10^6 query tokens: ~32 MB of work list): unsupported
+    assert f(16, 16, 16, qo.ctypes.data, qo.ctypes.data, 1, 1_000_000, 1_000_000, 128, 1,
+             0.1, 0, 16, 16, None) == 2
+    assert b"scratch" in lib.mla_last_error()
+    # the same checks as the workspace form
+    assert f(16, 16, 16, qo.ctypes.data, qo.ctypes.data, 1, 10, 10, 0, 1, 0.1, 0, 16, 16,
+             None) == 1                                        # num_heads
+    assert f(16, 16, 16, qo.ctypes.data, qo.ctypes.data, 5000, 10, 10, 4, 1, 0.1, 0, 16, 16,
+             None) == 1                                        # batch > 4096
+    assert f(16, 16, 16, qo.ctypes.data, qo.ctypes.data, 1, 10, 10, 4, 1, float("nan"), 0, 16,
+             16, None) == 1                                    # sm_scale
+    assert f(16, 16, 16, None, None, 1, 10, 10, 4, 1, 0.1, 0, 16, 16, None) == 1
+    assert f(None, None, None, None, None, 0, 0, 0, 4, 1, 0.1, 0, None, None, None) == 0
+    # the largest skewed workload fits: 128 heads, 262,144 tokens, 64 sequences
+    n = ctypes.c_int64()
+    assert lib.mla_device_plan_workspace_size(64, 262144, 128, 0, ctypes.byref(n)) == 0
+    assert n.value <= mra.NOALLOC_SCRATCH_BYTES
