@@ -106,7 +106,8 @@ def parse():
                     help="target CPU time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
-    ap.add_argument("--only", choices=["merge", "decompress", "absorbed", "decode", "fp32"],
+    ap.add_argument("--only", choices=["merge", "decompress", "absorbed", "decode", "fp32",
+                                       "skewed"],
                     default=None,
                     help="run only one secondary kernel (for profiling) and print its figures")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -192,6 +193,80 @@ def cpu_baseline(oracle, torch, x, target_s, seed=0):
             "kind": "oracle",
             "sample": f"{n} random query rows x {len(heads)} heads (heads {heads}) of the same "
                       f"batch, {pairs} visible pairs, {dt:.1f} s, fp64"}
+
+
+def _keys_seen(qo, kv, causal, t):
+    b = max(i for i in range(len(qo) - 1) if qo[i] <= t)
+    ql, kl = qo[b + 1] - qo[b], kv[b + 1] - kv[b]
+    i = t - qo[b]
+    return kl if not causal else min(kl, max(0, kl - ql + i + 1))
+
+
+def _cpu_note(oracle):
+    return {"cores": oracle.num_threads(), "nproc": os.cpu_count(), "kind": "oracle"}
+
+
+def oracle_sampled(oracle, torch, q, k, v, qo, kv, causal, sm_scale, num_heads, target_s,
+                   seed, extra_pairs_per_row=None, run_fn=None):
+    """Oracle wall time on seeded random query rows of one head, extrapolated
+    linearly in visible (row, key) pairs to every row and every head."""
+    rng = random.Random(seed)
+    h = rng.randrange(num_heads)
+    host = (q[:, h:h + 1].contiguous().cpu(), k[:, h:h + 1].contiguous().cpu(),
+            v[:, h:h + 1].contiguous().cpu())
+    total_pairs = visible_pairs(qo, kv, causal)
+
+    def run(n_rows):
+        rows = sorted(set(rng.randrange(qo[-1]) for _ in range(n_rows)))
+        pairs = sum(_keys_seen(qo, kv, causal, t) for t in rows)
+        if extra_pairs_per_row is not None:
+            pairs += extra_pairs_per_row * len(rows)
+        t0 = time.perf_counter()
+        if run_fn is not None:
+            run_fn(h, host, rows)
+        else:
+            oracle.prefill(*host, qo, kv, causal, sm_scale, rows)
+        return time.perf_counter() - t0, pairs, len(rows)
+
+    if run_fn is not None:
+        run_fn(h, host, [qo[-1] - 1])   # untimed: one-time set-up inside run_fn
+    dt, pairs, n = run(32)
+    n2 = max(32, min(100000, int(32 * target_s / max(dt, 1e-3))))
+    dt, pairs, n = run(n2)
+    if extra_pairs_per_row is not None:
+        total_pairs += extra_pairs_per_row * qo[-1]
+    full_s = dt * (total_pairs * num_heads) / max(pairs, 1)
+    out = {"sample": f"{n} seeded random query rows of head {h} (seed {seed}), {pairs} "
+                     f"visible pairs, fp64", "sample_s": round(dt, 3),
+           "sample_frac_of_work": pairs / (total_pairs * num_heads),
+           "extrapolated_full_s": round(full_s, 2),
+           "extrapolated": "linear in visible (row, key) pairs over every row and head"}
+    out.update(_cpu_note(oracle))
+    return out
+
+
+def oracle_tiny_full(oracle, torch, workloads):
+    """The tiny fp32 workload through the oracle in full, next to the GPU call."""
+    import mla_ragged_chunked_amd as mra
+    x = workloads.tiny_fp32()
+    t0 = time.perf_counter()
+    oracle.prefill(x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale)
+    cpu_s = time.perf_counter() - t0
+    g = [t.cuda() for t in (x.q, x.k, x.v)]
+    mra.ragged_prefill(*g, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        mra.ragged_prefill(*g, x.qo_indptr, x.kv_indptr, x.causal, x.sm_scale)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    out = {"workload": "tiny_fp32: lengths 1, 17, 64, 4 heads, fp32, causal",
+           "oracle_full_s": round(cpu_s, 5), "gpu_call_ms": round(sorted(ts)[10], 4)}
+    out.update(_cpu_note(oracle))
+    return out
 
 
 def time_merge(mra, torch, workloads, steps, warmup):
@@ -592,6 +667,14 @@ def main():
         print(json.dumps(time_decompress(mra, torch, workloads, args.steps, args.warmup,
                                          with_prefill=False)), flush=True)
         return
+    if args.only == "skewed":
+        xs = workloads.skewed_batch(device="cuda")
+        r = time_workload_prefill(
+            mra, torch, xs, args.steps, args.warmup,
+            f"skewed_batch: 64 log-uniform lengths [16, 32768], {xs.qo_indptr[-1]} tokens, 128 heads")
+        r["seq_lens"] = [xs.qo_indptr[i + 1] - xs.qo_indptr[i] for i in range(len(xs.qo_indptr) - 1)]
+        print(json.dumps(r), flush=True)
+        return
     if args.only == "fp32":
         print(json.dumps(time_fp32_prefill(mra, torch, workloads, args.steps, args.warmup)),
               flush=True)
@@ -661,6 +744,23 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: chunked prefill ...")
         sec["chunked_prefill"] = time_chunked(mra, torch, workloads, max(3, args.steps // 4), 1)
+        if args.cpu_seconds > 0:
+            import oracle
+            log("oracle: chunked prefill sample ...")
+            c = workloads.chunked_prefill(device="cuda")
+            m = c.main
+
+            def run_chunked(h, host, rows):
+                kvs = [(ch.k[:, h:h + 1].contiguous().cpu(), ch.v[:, h:h + 1].contiguous().cpu(),
+                        ch.kv_indptr) for ch in c.chunks]
+                oracle.chunked(host[0], host[1], host[2], m.qo_indptr, kvs, m.sm_scale, rows)
+
+            ctx_per_row = sum(ch.kv_indptr[-1] for ch in c.chunks) // len(c.chunks[0].kv_indptr[:-1])
+            sec["chunked_prefill"]["cpu_oracle"] = oracle_sampled(
+                oracle, torch, m.q, m.k, m.v, m.qo_indptr, m.kv_indptr, True, m.sm_scale,
+                m.num_heads, args.cpu_seconds / 3, seed=3, extra_pairs_per_row=ctx_per_row,
+                run_fn=run_chunked)
+            del c, m
         torch.cuda.empty_cache()
         log("secondary: paged context pass ...")
         sec["paged_context"] = time_paged_context(mra, torch, workloads, max(3, args.steps // 4), 1)
@@ -673,10 +773,46 @@ def main():
         # the lengths after the 262,144-token cap rule, as drawn
         sec["skewed_batch"]["seq_lens"] = [xs.qo_indptr[i + 1] - xs.qo_indptr[i]
                                            for i in range(len(xs.qo_indptr) - 1)]
+        if args.cpu_seconds > 0:
+            import oracle
+            log("oracle: skewed batch sample ...")
+            sec["skewed_batch"]["cpu_oracle"] = oracle_sampled(
+                oracle, torch, xs.q, xs.k, xs.v, xs.qo_indptr, xs.kv_indptr, True, xs.sm_scale,
+                xs.num_heads, args.cpu_seconds / 3, seed=4)
         del xs
         torch.cuda.empty_cache()
         log("secondary: decompression + prefill ...")
         sec["decompress_batch"] = time_decompress(mra, torch, workloads, max(3, args.steps // 4), 1)
+        if args.cpu_seconds > 0:
+            import oracle
+            log("oracle: decompression + prefill sample ...")
+            d = workloads.decompress_batch(device="cuda")
+            c_kv, k_rope = d.c_kv.cpu(), d.k_rope.cpu()
+            dec = {}
+
+            def run_dec(h, host, rows):
+                # the decompression of head h (every token) is timed once and
+                # kept; each sample then times the prefill rows alone
+                if h not in dec:
+                    t0 = time.perf_counter()
+                    wk = d.w_uk[:, h * 128:(h + 1) * 128].contiguous().cpu()
+                    wv = d.w_uv[:, h * 128:(h + 1) * 128].contiguous().cpu()
+                    rk, rv = oracle.decompress(c_kv, k_rope, wk, wv, 1)
+                    dec[h] = (rk, rv, time.perf_counter() - t0)
+                rk, rv, _ = dec[h]
+                oracle.prefill(host[0].double(), rk, rv, d.indptr, d.indptr, True, d.sm_scale, rows)
+
+            # K and V stand in for the decompressed ones (only their shapes are used)
+            r = oracle_sampled(oracle, torch, d.q, d.q, d.q[:, :, :128], d.indptr, d.indptr,
+                               True, d.sm_scale, d.num_heads, args.cpu_seconds / 3, seed=5,
+                               run_fn=run_dec)
+            dec_s = next(iter(dec.values()))[2]
+            r["decompress_one_head_s"] = round(dec_s, 3)
+            r["extrapolated_full_s"] = round(r["extrapolated_full_s"] + dec_s * d.num_heads, 2)
+            r["extrapolated"] = ("prefill linear in visible (row, key) pairs over every row and "
+                                 "head, plus the one-head decompression time x heads")
+            sec["decompress_batch"]["cpu_oracle"] = r
+            del d, c_kv, k_rope
         torch.cuda.empty_cache()
         log("secondary: absorbed prefill over the latent cache ...")
         sec["absorbed_batch"] = time_absorbed(mra, torch, workloads, max(3, args.steps // 4), 1)
@@ -687,6 +823,9 @@ def main():
         log("secondary: fp32 prefill ...")
         sec["fp32_prefill"] = time_fp32_prefill(mra, torch, workloads, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
+        if args.cpu_seconds > 0:
+            import oracle
+            sec["tiny_fp32"] = oracle_tiny_full(oracle, torch, workloads)
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
 
