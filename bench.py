@@ -107,7 +107,7 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--n-xcd", type=int, default=8)
     ap.add_argument("--only", choices=["merge", "decompress", "absorbed", "decode", "fp32",
-                                       "skewed"],
+                                       "skewed", "fused"],
                     default=None,
                     help="run only one secondary kernel (for profiling) and print its figures")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -522,6 +522,125 @@ def time_decompress(mra, torch, workloads, steps, warmup, with_prefill=True):
     return out
 
 
+def fused_key_tiles(qo, kv, causal, block_m=128, block_n=32):
+    """32-key tiles the fused kernel decompresses per head: every 128-row
+    query tile decompresses each key tile it visits."""
+    n = 0
+    for b in range(len(qo) - 1):
+        ql, kl = qo[b + 1] - qo[b], kv[b + 1] - kv[b]
+        for r0 in range(0, ql, block_m):
+            rows = min(block_m, ql - r0)
+            hi = min(kl, max(0, kl - ql + r0 + rows)) if causal else kl
+            n += -(-hi // block_n)
+    return n
+
+
+def time_fused_decompress(mra, torch, workloads, steps, warmup, extras=True):
+    """Decompression fused into the prefill on the decompression workload
+    (8 x 4096 tokens, 128 heads, causal), and the absorbed kernel on the same
+    lengths. The fused kernel's MFMA work is the attention plus the
+    decompression of every key tile once per query tile that visits it."""
+    d = workloads.decompress_batch(device="cuda")
+    H = d.num_heads
+    o, lse = mra.decompress_prefill(d.q, d.c_kv, d.k_rope, d.w_uk, d.w_uv, d.indptr, d.indptr,
+                                    True, d.sm_scale)
+    args = (d.q, d.c_kv, d.k_rope, d.w_uk, d.w_uv, d.indptr, d.indptr, True, d.sm_scale)
+    for _ in range(warmup):
+        mra.decompress_prefill(*args, out=o, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mra.decompress_prefill(*args, out=o, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = visible_pairs(d.indptr, d.indptr, True)
+    attn_flops = 2.0 * H * pairs * 320
+    tiles = fused_key_tiles(d.indptr, d.indptr, True)
+    dec_flops = 2.0 * 2 * 32 * 512 * 128 * tiles * H
+    mfma = (attn_flops + dec_flops) / ms / 1e9
+    fused = {"fused_ms": round(ms, 4),
+             "attention_TFLOP/s": round(attn_flops / ms / 1e9, 1),
+             "decompressed_key_tiles_per_head": tiles,
+             "mfma_flop": attn_flops + dec_flops,
+             "roofline": {"bound": "mfma", "achieved": round(mfma, 1), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(mfma / PEAK_BF16_TFLOPS, 4),
+                          "traffic": profile_traffic("decompress_prefill_fused_8x4096_128heads.txt",
+                                                     "mla_ragged_chunked_amd/csrc/decompress_prefill.hip"),
+                          "kernel": "decompress_prefill_kernel"}}
+    del o, lse, d
+    torch.cuda.empty_cache()
+    if not extras:
+        return fused, None
+    # the absorbed kernel on the same lengths (its query and output projections,
+    # Q_nope W_UK^T and O_latent W_UV, are extra GEMMs outside this kernel)
+    lens = [4096] * 8
+    x = workloads.absorbed_inputs(lens, lens, H, seed=6, causal=True, device="cuda")
+    out, alse = mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale)
+    for _ in range(warmup):
+        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale, out=out,
+                             lse=alse)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        mra.absorbed_prefill(x.q, x.kv, x.qo_indptr, x.kv_indptr, True, x.sm_scale, out=out,
+                             lse=alse)
+    e1.record()
+    torch.cuda.synchronize()
+    ams = e0.elapsed_time(e1) / steps
+    aflops = 2.0 * H * pairs * (576 + 512)
+    absorbed = {"absorbed_ms": round(ams, 4), "absorbed_TFLOP/s": round(aflops / ams / 1e9, 1),
+                "projection_flop_outside_kernel": 2.0 * 2 * x.q.shape[0] * H * 128 * 512}
+    del out, alse, x
+    torch.cuda.empty_cache()
+    fused["short_chunks"] = time_fused_short_chunks(mra, torch, workloads, steps, warmup)
+    return fused, absorbed
+
+
+def time_fused_short_chunks(mra, torch, workloads, steps, warmup, n_req=16, new=128,
+                            prefix=4096, H=128):
+    """Where each key tile is visited by one query tile only: n_req requests
+    of `new` query tokens over their own `prefix` + `new` keys (bottom-right
+    causal). The two-call path decompresses every key token to HBM and then
+    runs the prefill; the fused kernel decompresses each key tile once on chip."""
+    x = workloads.latent_prefill_inputs([new] * n_req, [prefix + new] * n_req, H, seed=13,
+                                        causal=True, device="cuda")
+    tk = x.c_kv.shape[0]
+
+    def timed(fn):
+        fn()
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    o = torch.empty((x.q.shape[0], H, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((x.q.shape[0], H), dtype=torch.float32, device="cuda")
+    fused_ms = timed(lambda: mra.decompress_prefill(x.q, x.c_kv, x.k_rope, x.w_uk, x.w_uv,
+                                                    x.qo_indptr, x.kv_indptr, True, x.sm_scale,
+                                                    out=o, lse=lse))
+    k = torch.empty((tk, H, 192), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((tk, H, 128), dtype=torch.bfloat16, device="cuda")
+    dec_ms = timed(lambda: mra.decompress_kv(x.c_kv, x.k_rope, x.w_uk, x.w_uv, H, k_out=k,
+                                             v_out=v))
+    pre_ms = timed(lambda: mra.ragged_prefill(x.q, k, v, x.qo_indptr, x.kv_indptr, True,
+                                              x.sm_scale, out=o, lse=lse))
+    del x, o, lse, k, v
+    torch.cuda.empty_cache()
+    return {"workload": f"{n_req} requests x {new} new tokens over {prefix} + {new} keys, "
+                        f"{H} heads, causal",
+            "fused_ms": round(fused_ms, 4), "two_call_decompress_ms": round(dec_ms, 4),
+            "two_call_prefill_ms": round(pre_ms, 4),
+            "two_call_end_to_end_ms": round(dec_ms + pre_ms, 4)}
+
+
 def time_absorbed(mra, torch, workloads, steps, warmup):
     """Weight-absorbed prefill over the latent cache on the DeepSeek-V3 batch
     lengths: 576-dim absorbed queries, 576-dim shared cache rows, 512-dim
@@ -666,6 +785,12 @@ def main():
     if args.only == "decompress":
         print(json.dumps(time_decompress(mra, torch, workloads, args.steps, args.warmup,
                                          with_prefill=False)), flush=True)
+        return
+    if args.only == "fused":
+        # the fused kernel on the decompression workload alone (for profiling)
+        fused, _ = time_fused_decompress(mra, torch, workloads, args.steps, args.warmup,
+                                         extras=False)
+        print(json.dumps(fused), flush=True)
         return
     if args.only == "skewed":
         xs = workloads.skewed_batch(device="cuda")
@@ -814,6 +939,10 @@ def main():
             sec["decompress_batch"]["cpu_oracle"] = r
             del d, c_kv, k_rope
         torch.cuda.empty_cache()
+        log("secondary: decompression fused into the prefill ...")
+        fused, absorbed = time_fused_decompress(mra, torch, workloads, max(3, args.steps // 4), 1)
+        sec["decompress_batch"]["fused"] = fused
+        sec["decompress_batch"]["absorbed_same_lengths"] = absorbed
         log("secondary: absorbed prefill over the latent cache ...")
         sec["absorbed_batch"] = time_absorbed(mra, torch, workloads, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()

@@ -328,6 +328,35 @@ int mla_decompress_kv(const void *c_kv, const void *k_rope, const void *w_uk, co
                       void *stream);
 
 /*
+ * Ragged MLA prefill with the decompression above fused into the attention
+ * kernel (the other answer to sglang issue 3849's question: decompress the
+ * latent per key tile on chip instead of writing K/V to HBM). The result is
+ * mla_decompress_kv followed by mla_ragged_prefill (bf16, same indptrs and
+ * causal rule), up to the order of fp32 additions: K and V are rounded to
+ * bf16 before the attention uses them, exactly as the two-call path stores
+ * them. Every query tile of 128 rows decompresses each 32-key tile it
+ * visits again, so the decompression work grows with the query length; the
+ * benchmark measures this against the two-call path and the absorbed path.
+ *
+ *   q        device bf16 [Tq, H, 192], Tq = qo_indptr[batch].
+ *   c_kv     device bf16 [Tk, 512], k_rope device bf16 [Tk, 64]
+ *            (Tk = kv_indptr[batch]; key j of sequence b is row kv_indptr[b] + j).
+ *   w_uk, w_uv device bf16 [512, H*128] (column h*128+d is head h, dim d).
+ *   qo_indptr, kv_indptr  host int32 [batch+1], as for mla_ragged_prefill.
+ *   out      device bf16 [Tq, H, 128]; lse device fp32 [Tq, H] or NULL.
+ *   num_heads in [1, 65535]; causal 0 or 1 (bottom-right aligned);
+ *   sm_scale finite and > 0. All device pointers 16-byte aligned.
+ * Rows that see no key get O = 0 and LSE = -inf. The call keeps a device
+ * work list per (device, stream), grown as needed and freed at exit.
+ * Returns MLA_EINVAL for bad arguments (before any HIP call), MLA_EUNSUPPORTED
+ * when Tq x H or Tk x H exceeds 2^31, MLA_ENOMEM, or MLA_EHIP.
+ */
+int mla_decompress_prefill(const void *q, const void *c_kv, const void *k_rope, const void *w_uk,
+                           const void *w_uv, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                           int32_t batch, int32_t num_heads, int32_t causal, float sm_scale,
+                           void *out, float *lse, void *stream);
+
+/*
  * Weight-absorbed MLA prefill over the latent cache (sglang issue 3849,
  * "[DeepseekR1] How ragged prefill manage kv_cache?": the absorb path that
  * attends the compressed cache directly instead of decompressing it). Each

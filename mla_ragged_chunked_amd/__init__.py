@@ -23,7 +23,7 @@ import numpy as np
 import torch
 
 __all__ = ["ragged_prefill", "ragged_prefill_paged", "ragged_prefill_device_plan_noalloc",
-           "merge_state", "decompress_kv",
+           "merge_state", "decompress_kv", "decompress_prefill",
            "absorbed_prefill", "absorbed_prefill_paged", "absorbed_plan_items", "AbsorbedPlan", "Plan", "DevicePlan", "MlaError", "lib",
            "LIB_PATH", "DQK", "DVO", "DLAT", "DROPE", "PREFILL_BLOCK_M", "EXPORTED_SYMBOLS"]
 
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = [
     "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
     "mla_ragged_prefill_device_plan", "mla_ragged_prefill_device_plan_noalloc",
     "mla_ragged_prefill_paged",
-    "mla_merge_state", "mla_decompress_kv", "mla_absorbed_prefill", "mla_absorbed_plan_items",
+    "mla_merge_state", "mla_decompress_kv", "mla_decompress_prefill", "mla_absorbed_prefill", "mla_absorbed_plan_items",
     "mla_absorbed_prefill_paged", "mla_absorbed_plan_create", "mla_absorbed_plan_destroy",
     "mla_absorbed_plan_build", "mla_absorbed_plan_upload", "mla_absorbed_run",
     "mla_absorbed_run_paged", "mla_absorbed_plan_info",
@@ -95,6 +95,7 @@ def lib():
                                       P, P], ctypes.c_int),
         "mla_merge_state": ([P, P, P, P, P, P, I64, I32, I32, P], ctypes.c_int),
         "mla_decompress_kv": ([P, P, P, P, I64, I32, P, P, P], ctypes.c_int),
+        "mla_decompress_prefill": ([P, P, P, P, P, P, P, I32, I32, I32, F, P, P, P], ctypes.c_int),
         "mla_absorbed_prefill": ([P, P, P, P, I32, I32, I32, F, P, P, P], ctypes.c_int),
         "mla_absorbed_plan_items": ([P, P, I32, I32, I32, P, I64, ctypes.POINTER(I64)],
                                     ctypes.c_int),
@@ -440,6 +441,54 @@ def decompress_kv(c_kv: torch.Tensor, k_rope: torch.Tensor, w_uk: torch.Tensor,
                                        _stream(c_kv.device)),
                "mla_decompress_kv")
     return k_out, v_out
+
+
+def decompress_prefill(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor,
+                       w_uk: torch.Tensor, w_uv: torch.Tensor, qo_indptr, kv_indptr,
+                       causal: bool, sm_scale: float, return_lse: bool = True,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Ragged MLA prefill with the K/V decompression fused into the kernel:
+    q [Tq,H,192], c_kv [Tk,512], k_rope [Tk,64], w_uk / w_uv [512,H*128], all
+    bf16 on the GPU; host int indptrs of length batch+1. Equals decompress_kv
+    followed by ragged_prefill. Returns out [Tq,H,128] bf16 (and lse [Tq,H]
+    fp32, natural log) on the current stream."""
+    for t, name in ((q, "q"), (c_kv, "c_kv"), (k_rope, "k_rope"), (w_uk, "w_uk"), (w_uv, "w_uv")):
+        _dev_tensor(t, name)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    qo, kv = _indptr(qo_indptr), _indptr(kv_indptr)
+    if len(qo) != len(kv) or len(qo) < 1:
+        raise ValueError("qo_indptr and kv_indptr must have the same length >= 1")
+    if q.dim() != 3 or q.shape[2] != DQK:
+        raise ValueError("q must be [tokens, heads, 192]")
+    tq, heads = q.shape[0], q.shape[1]
+    tk = c_kv.shape[0]
+    if c_kv.shape != (tk, DLAT) or k_rope.shape != (tk, DROPE):
+        raise ValueError("c_kv must be [Tk,512] and k_rope [Tk,64]")
+    if w_uk.shape != (DLAT, heads * DVO) or w_uv.shape != (DLAT, heads * DVO):
+        raise ValueError("w_uk / w_uv must be [512, H*128]")
+    if qo[-1] != tq or kv[-1] != tk:
+        raise ValueError("indptr totals do not match the token counts of q / c_kv")
+    if out is None:
+        out = torch.empty((tq, heads, DVO), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((tq, heads), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, "out")
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (tq, heads, DVO):
+        raise ValueError("out must be bf16 [Tq, H, 128]")
+    if return_lse:
+        _dev_tensor(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (tq, heads):
+            raise ValueError("lse must be fp32 [tokens, heads]")
+    with torch.cuda.device(q.device):
+        _check(lib().mla_decompress_prefill(_ptr(q), _ptr(c_kv), _ptr(k_rope), _ptr(w_uk),
+                                            _ptr(w_uv), qo.ctypes.data, kv.ctypes.data,
+                                            len(qo) - 1, heads, int(bool(causal)),
+                                            float(sm_scale), _ptr(out),
+                                            _ptr(lse) if return_lse else None,
+                                            _stream(q.device)),
+               "mla_decompress_prefill")
+    return (out, lse) if return_lse else out
 
 
 def absorbed_plan_items(qo_indptr, kv_indptr, num_heads: int, causal: bool) -> np.ndarray:

@@ -24,13 +24,19 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # the LDS DMA asm in the prefill kernel declares M0 clobbered on purpose
           "-Wno-inline-asm"]
 SOURCES = ["abi.cpp", "planner.cpp", "prefill_bf16.hip", "prefill_fp32.hip", "merge.hip",
-           "decompress.hip", "device_plan.hip", "prefill_absorbed.hip"]
+           "decompress.hip", "device_plan.hip", "prefill_absorbed.hip", "decompress_prefill.hip"]
+# Per-source flags. The fused decompression + prefill kernel holds 256
+# registers of weights per lane; with MFMA results in VGPRs those weights
+# fill the AGPRs as MFMA sources and nothing is copied between the two
+# files or spilled (the default form keeps results in AGPRs and spills).
+SOURCE_FLAGS = {"decompress_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *SOURCE_FLAGS.get(src, []), *extra, *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -6,6 +6,7 @@
 // mla_last_error(). No exception escapes.
 #include "../../include/mla_ragged.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -665,6 +666,36 @@ int device_plan_call(const void* q, const void* k, const void* v, const int32_t*
     return MLA_OK;
 }
 
+// Fused decompression + prefill: the query tiles of all sequences (one head
+// each), sorted by the keys they visit, heaviest first. n_busy = tiles that
+// see at least one key (a prefix of the list).
+int fused_tiles(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t causal,
+                std::vector<WorkItem>& tiles, int64_t& n_busy) {
+    std::string err;
+    try {
+        if (!mla::build_work_list(qo, kv, batch, 1, causal != 0, mla::decompress_prefill_block_m(),
+                                  1, 1, tiles, err))
+            return fail(MLA_EINVAL, err);
+    } catch (const std::bad_alloc&) {
+        return fail(MLA_ENOMEM, "host allocation of the work list failed");
+    }
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const WorkItem& a, const WorkItem& b) { return a.kv_hi > b.kv_hi; });
+    n_busy = std::count_if(tiles.begin(), tiles.end(), [](const WorkItem& t) { return t.kv_hi > 0; });
+    return MLA_OK;
+}
+
+// Per (device, stream): the device copy of the tile list and the fence of
+// the last run that read it.
+struct FusedState {
+    std::mutex mu;
+    RunFence last_run;
+    DeviceWorkList<WorkItem> dwl;
+    ~FusedState() { last_run.wait(); }   // before the members free the list
+};
+std::mutex g_fused_mu;
+std::map<std::pair<int, void*>, FusedState*>* g_fused = nullptr;
+
 }  // namespace
 
 extern "C" {
@@ -861,6 +892,60 @@ int mla_decompress_kv(const void* c_kv, const void* k_rope, const void* w_uk, co
                                           v_out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decompression kernel launch");
     return MLA_OK;
+}
+
+int mla_decompress_prefill(const void* q, const void* c_kv, const void* k_rope, const void* w_uk,
+                           const void* w_uv, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                           int32_t batch, int32_t num_heads, int32_t causal, float sm_scale,
+                           void* out, float* lse, void* stream) {
+    if (int s = check_scale(sm_scale)) return s;
+    if (batch < 0) return fail(MLA_EINVAL, "batch must be >= 0");
+    if (num_heads < 1 || num_heads > 65535) return fail(MLA_EINVAL, "num_heads must be in [1, 65535]");
+    if (causal != 0 && causal != 1) return fail(MLA_EINVAL, "causal must be 0 or 1");
+    if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
+        return fail(MLA_EINVAL, "indptr is NULL");
+    std::vector<WorkItem> tiles;
+    int64_t n_busy = 0;
+    if (int s = fused_tiles(qo_indptr, kv_indptr, batch, causal, tiles, n_busy)) return s;
+    const int64_t tq = batch > 0 ? qo_indptr[batch] : 0;
+    const int64_t tk = batch > 0 ? kv_indptr[batch] : 0;
+    if (tq * num_heads > INT32_MAX || tk * num_heads > INT32_MAX)
+        return fail(MLA_EUNSUPPORTED, "tokens x heads exceeds 2^31 rows");
+    if (tq > 0 && (q == nullptr || out == nullptr))
+        return fail(MLA_EINVAL, "q and out must be non-NULL when there are query rows");
+    if (n_busy > 0 && (!c_kv || !k_rope || !w_uk || !w_uv))
+        return fail(MLA_EINVAL, "c_kv, k_rope, w_uk and w_uv must be non-NULL when keys are visible");
+    if (!aligned16(q) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) ||
+        !aligned16(w_uv) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
+        return fail(MLA_EINVAL, "all device pointers must be 16-byte aligned");
+    if (tiles.empty()) return MLA_OK;
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    FusedState* st = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_fused_mu);
+        if (g_fused == nullptr) g_fused = new (std::nothrow) std::map<std::pair<int, void*>, FusedState*>();
+        if (g_fused == nullptr) return fail(MLA_ENOMEM, "fused state table");
+        auto key = std::make_pair(dev, stream);
+        auto it = g_fused->find(key);
+        if (it == g_fused->end()) {
+            st = new (std::nothrow) FusedState();
+            if (st == nullptr) return fail(MLA_ENOMEM, "fused state");
+            (*g_fused)[key] = st;
+        } else {
+            st = it->second;
+        }
+    }
+    // threads that share the stream take turns from the upload to the launch
+    std::lock_guard<std::mutex> state_lock(st->mu);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int r = st->dwl.upload(tiles, s, [st] { st->last_run.wait(); })) return r;
+    e = mla::launch_decompress_prefill(st->dwl.dev, static_cast<int64_t>(tiles.size()), n_busy, q,
+                                       c_kv, k_rope, w_uk, w_uv, out, lse, num_heads, sm_scale, s);
+    if (e != hipSuccess) return hip_fail(e, "fused decompression + prefill kernel launch");
+    return st->last_run.record(s);
 }
 
 int mla_absorbed_plan_items(const int32_t* qo_indptr, const int32_t* kv_indptr, int32_t batch,

@@ -144,6 +144,14 @@ hipError_t launch_merge_splits(const float* part_o, const float* part_lse, int s
 hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b,
                         const float* lse_b, void* o, float* lse, int64_t num_rows,
                         int dtype_bf16, hipStream_t stream);
+// Decompression fused into the prefill: `tiles` are query tiles of
+// decompress_prefill_block_m() rows (one head each, head fields unused)
+// sorted by kv_hi, heaviest first; the first n_busy have kv_hi > 0.
+int decompress_prefill_block_m();
+hipError_t launch_decompress_prefill(const WorkItem* tiles, int64_t n_tiles, int64_t n_busy,
+                                     const void* q, const void* c_kv, const void* k_rope,
+                                     const void* w_uk, const void* w_uv, void* out, float* lse,
+                                     int num_heads, float sm_scale, hipStream_t stream);
 hipError_t launch_decompress(const void* c_kv, const void* k_rope, const void* w_uk,
                              const void* w_uv, int64_t num_tokens, int num_heads,
                              void* k_out, void* v_out, hipStream_t stream);

@@ -42,6 +42,12 @@ hipError_t launch_decompress(const void*, const void*, const void*, const void*,
                              void*, void*, hipStream_t) {
     return hipErrorInvalidValue;
 }
+int decompress_prefill_block_m() { return 128; }
+hipError_t launch_decompress_prefill(const WorkItem*, int64_t, int64_t, const void*, const void*,
+                                     const void*, const void*, const void*, void*, float*, int,
+                                     float, hipStream_t) {
+    return hipErrorInvalidValue;
+}
 int64_t device_plan_max_items(int batch, int64_t max_tq, int num_heads, int block_m) {
     return 8LL * ((num_heads + 7) / 8) * ((max_tq + block_m - 1) / block_m + batch);
 }
@@ -135,6 +141,12 @@ int main() {
                                    nullptr, nullptr, nullptr) != MLA_OK;
     checks += mla_merge_state(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 10, 128,
                               MLA_DTYPE_BF16, nullptr) != MLA_OK;
+    checks += mla_decompress_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, bad_qo.data(),
+                                     ok_kv.data(), 2, 4, 1, 0.1f, nullptr, nullptr,
+                                     nullptr) == MLA_EINVAL;
+    checks += mla_decompress_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, ok_kv.data(),
+                                     ok_kv.data(), 2, 4, 1, 0.1f, nullptr, nullptr,
+                                     nullptr) == MLA_EINVAL;   // NULL tensors
     // the allocation-free device plan: oversize and invalid calls fail on the host
     static int32_t dummy[64];
     checks += mla_ragged_prefill_device_plan_noalloc(dummy, dummy, dummy, ok_kv.data(),

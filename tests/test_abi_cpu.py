@@ -509,6 +509,12 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         mra.absorbed_prefill(torch.zeros((t, h, 576), dtype=torch.bfloat16),
                              torch.zeros((t, 576), dtype=torch.bfloat16), ind, ind, True, 0.1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mra.decompress_prefill(q, torch.zeros((t, 512), dtype=torch.bfloat16),
+                               torch.zeros((t, 64), dtype=torch.bfloat16),
+                               torch.zeros((512, h * 128), dtype=torch.bfloat16),
+                               torch.zeros((512, h * 128), dtype=torch.bfloat16), ind, ind,
+                               True, 0.1)
 
 
 def test_binding_block_m_matches_the_planner():
@@ -540,3 +546,39 @@ def test_noalloc_prefill_rejects_bad_calls_before_any_hip_call():
     n = ctypes.c_int64()
     assert lib.mla_device_plan_workspace_size(64, 262144, 128, 0, ctypes.byref(n)) == 0
     assert n.value <= mra.NOALLOC_SCRATCH_BYTES
+
+
+def test_decompress_prefill_rejects_invalid_arguments_before_any_hip_call():
+    lib = mra.lib()
+    qo = np.array([0, 4], dtype=np.int32)
+    kv = np.array([0, 4], dtype=np.int32)
+    def call(**kw):
+        a = dict(q=16, c=16, r=16, wk=16, wv=16, qo=qo.ctypes.data, kvp=kv.ctypes.data, batch=1,
+                 heads=2, causal=1, scale=0.1, out=16, lse=16)
+        a.update(kw)
+        return lib.mla_decompress_prefill(a["q"], a["c"], a["r"], a["wk"], a["wv"], a["qo"],
+                                          a["kvp"], a["batch"], a["heads"], a["causal"],
+                                          a["scale"], a["out"], a["lse"], None)
+    assert call(scale=0.0) == 1
+    assert call(scale=float("inf")) == 1
+    assert call(heads=0) == 1
+    assert call(heads=70000) == 1
+    assert call(causal=-1) == 1
+    assert call(batch=-1) == 1
+    assert call(qo=None) == 1
+    for name in ("q", "c", "r", "wk", "wv", "out"):
+        assert call(**{name: None}) == 1, name
+    for name in ("q", "c", "r", "wk", "wv", "out", "lse"):
+        assert call(**{name: 24}) == 1, name              # misaligned
+    assert call(qo=np.array([0, 4, 2], dtype=np.int32).ctypes.data,
+                kvp=np.array([0, 1, 2], dtype=np.int32).ctypes.data, batch=2) == 1
+    assert call(kvp=np.array([2, 4], dtype=np.int32).ctypes.data) == 1   # indptr[0] != 0
+    big = np.array([0, 1 << 24], dtype=np.int32)
+    assert call(qo=big.ctypes.data, heads=256) == 2       # tokens x heads >= 2^31
+    # nothing to do: returns before any HIP call
+    empty = np.array([0], dtype=np.int32)
+    assert call(qo=empty.ctypes.data, kvp=empty.ctypes.data, batch=0, q=None, c=None, r=None,
+                wk=None, wv=None, out=None, lse=None) == 0
+    # query rows but no keys at all still need q and out, not the latent inputs
+    nokeys = np.array([0, 0], dtype=np.int32)
+    assert call(kvp=nokeys.ctypes.data, q=None) == 1

@@ -600,6 +600,91 @@ def test_decompress_then_prefill_full_size():
               f"decompress+prefill head {h}")
 
 
+# ---------------------------------------------------------------------------
+# decompression fused into the prefill
+# ---------------------------------------------------------------------------
+
+def _latent_to(x: workloads.LatentPrefillInputs, device):
+    return workloads.LatentPrefillInputs(
+        x.c_kv.to(device), x.k_rope.to(device), x.w_uk.to(device), x.w_uv.to(device),
+        x.q.to(device), x.qo_indptr, x.kv_indptr, x.num_heads, x.causal, x.sm_scale)
+
+
+FUSED_CASES = [
+    # (query lengths, key lengths, heads, causal)
+    ([1, 31, 32, 33, 127, 128, 129, 257], [1, 31, 32, 33, 127, 128, 129, 257], 3, True),
+    ([1, 31, 32, 33, 127, 128, 129, 257], [1, 31, 32, 33, 127, 128, 129, 257], 3, False),
+    ([5, 130, 64], [300, 130, 1000], 2, True),       # queries after a prefix
+    ([5, 130, 64], [300, 130, 1000], 2, False),
+    ([200, 40, 7], [64, 0, 7], 1, True),              # rows that see no key, an empty key range
+    ([0, 70, 0, 3], [10, 70, 0, 0], 4, True),         # empty sequences
+    ([33, 65, 300], [33, 65, 300], 128, True),        # 128 heads, two parts per head
+    ([1000], [1000], 5, True),                        # one sequence, many tiles per workgroup
+]
+
+
+@pytest.mark.parametrize("lens_q,lens_kv,heads,causal", FUSED_CASES)
+def test_decompress_prefill_small_parity(lens_q, lens_kv, heads, causal):
+    x = workloads.latent_prefill_inputs(lens_q, lens_kv, heads, seed=11, causal=causal)
+    g = _latent_to(x, DEV)
+    _flush(f"[gpu] fused decompress+prefill q={lens_q} kv={lens_kv} H={heads} causal={causal}")
+    o, lse = mra.decompress_prefill(g.q, g.c_kv, g.k_rope, g.w_uk, g.w_uv, x.qo_indptr,
+                                    x.kv_indptr, causal, x.sm_scale)
+    # the two-call path on the same bytes
+    k, v = mra.decompress_kv(g.c_kv, g.k_rope, g.w_uk, g.w_uv, heads)
+    o2, lse2 = mra.ragged_prefill(g.q, k, v, x.qo_indptr, x.kv_indptr, causal, x.sm_scale)
+    torch.cuda.synchronize()
+    rk, rv = oracle.decompress(x.c_kv, x.k_rope, x.w_uk, x.w_uv, heads)     # fp64
+    ro, rl = oracle.prefill(x.q.double(), rk, rv, x.qo_indptr, x.kv_indptr, causal, x.sm_scale)
+    check(o, lse, ro, rl, torch.bfloat16, "fused decompress+prefill")
+    # both GPU paths round K/V to bf16 the same way: they agree to within the
+    # order of their fp32 sums
+    check(o, lse, o2.double().cpu(), lse2.double().cpu(), torch.bfloat16, "fused vs two-call")
+
+
+def test_decompress_prefill_without_lse():
+    x = workloads.latent_prefill_inputs([70, 9], [100, 9], 2, seed=12, causal=True)
+    g = _latent_to(x, DEV)
+    o, lse = mra.decompress_prefill(g.q, g.c_kv, g.k_rope, g.w_uk, g.w_uv, x.qo_indptr,
+                                    x.kv_indptr, True, x.sm_scale)
+    o_only = mra.decompress_prefill(g.q, g.c_kv, g.k_rope, g.w_uk, g.w_uv, x.qo_indptr,
+                                    x.kv_indptr, True, x.sm_scale, return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_only)
+
+
+def test_decompress_prefill_full_size():
+    d = workloads.decompress_batch(device=DEV)
+    H = d.num_heads
+    _flush(f"[gpu] fused decompress+prefill, decompress_batch T={d.indptr[-1]} H={H}")
+    o, lse = mra.decompress_prefill(d.q, d.c_kv, d.k_rope, d.w_uk, d.w_uv, d.indptr, d.indptr,
+                                    True, d.sm_scale)
+    torch.cuda.synchronize()
+    _row_properties(o, lse)
+    c_kv, k_rope = d.c_kv.cpu(), d.k_rope.cpu()
+    rows = sample_rows(d.indptr, block=mra.PREFILL_BLOCK_M, n_random=32, seed=5)
+    idx = torch.tensor(rows)
+    for h in (0, 3, H - 2, H - 1):
+        wk = d.w_uk[:, h * 128:(h + 1) * 128].contiguous().cpu()
+        wv = d.w_uv[:, h * 128:(h + 1) * 128].contiguous().cpu()
+        rk, rv = oracle.decompress(c_kv, k_rope, wk, wv, 1)           # fp64, all tokens
+        qh = head_slice(d.q, h).double()
+        ro, rl = oracle.prefill(qh, rk, rv, d.indptr, d.indptr, True, d.sm_scale, rows)
+        check(o[idx, h:h + 1].cpu(), lse[idx, h:h + 1].cpu(), ro, rl, torch.bfloat16,
+              f"fused decompress+prefill head {h}")
+    # every row and head against the two-call path
+    k, v = mra.decompress_kv(d.c_kv, d.k_rope, d.w_uk, d.w_uv, H)
+    o2, lse2 = mra.ragged_prefill(d.q, k, v, d.indptr, d.indptr, True, d.sm_scale)
+    torch.cuda.synchronize()
+    del k, v
+    err_o = (o.float() - o2.float()).abs().max().item()
+    err_l = (lse - lse2).abs().max().item()
+    _flush(f"[gpu] fused vs two-call, all rows: O {err_o:.3e}, LSE {err_l:.3e}")
+    assert err_o <= TOL[torch.bfloat16][0] and err_l <= TOL[torch.bfloat16][1]
+    del d, o, lse, o2, lse2
+    torch.cuda.empty_cache()
+
+
 def _paged_cache_on_gpu(k, v, kv_indptr, page, seed):
     """Page pools [P, page, H, D] holding the contiguous K/V of every sequence
     in a seeded random page order (plus two pages of zeros), built on the GPU,

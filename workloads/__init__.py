@@ -90,6 +90,22 @@ class DecompressInputs:
     sm_scale: float
 
 
+@dataclass
+class LatentPrefillInputs:
+    """A ragged prefill whose K/V come from the latent cache: c_kv, k_rope and
+    the up-projections, with separate query and key lengths."""
+    c_kv: torch.Tensor                 # [Tk, 512]
+    k_rope: torch.Tensor               # [Tk, 64]
+    w_uk: torch.Tensor                 # [512, H*128]
+    w_uv: torch.Tensor                 # [512, H*128]
+    q: torch.Tensor                    # [Tq, H, 192]
+    qo_indptr: List[int]
+    kv_indptr: List[int]
+    num_heads: int
+    causal: bool
+    sm_scale: float
+
+
 def indptr_from_lengths(lengths) -> List[int]:
     out = [0]
     for n in lengths:
@@ -227,6 +243,25 @@ def decompress_batch(device="cpu", num_seqs: int = 8, seq_len: int = 4096,
     return DecompressInputs(c_kv, k_rope, w_uk, w_uv, q,
                             indptr_from_lengths([seq_len] * num_seqs), num_heads,
                             default_sm_scale())
+
+
+def latent_prefill_inputs(lengths_q, lengths_kv, num_heads: int, seed: int, causal: bool = True,
+                          device="cpu") -> LatentPrefillInputs:
+    """The decompression workload's distributions (c_kv, k_rope ~ N(0,1),
+    W_UK, W_UV ~ N(0, 1/512), Q ~ N(0,1), all bf16, drawn in that order) for
+    a ragged batch with separate query and key lengths."""
+    g = _gen(seed, device)
+    qo = indptr_from_lengths(lengths_q)
+    kv = indptr_from_lengths(lengths_kv)
+    bf = torch.bfloat16
+    c_kv = randn((kv[-1], D_LATENT), g, bf, device)
+    k_rope = randn((kv[-1], D_ROPE), g, bf, device)
+    std = 1.0 / math.sqrt(D_LATENT)
+    w_uk = randn((D_LATENT, num_heads * D_NOPE), g, bf, device, std=std)
+    w_uv = randn((D_LATENT, num_heads * DVO), g, bf, device, std=std)
+    q = randn((qo[-1], num_heads, DQK), g, bf, device)
+    return LatentPrefillInputs(c_kv, k_rope, w_uk, w_uv, q, qo, kv, num_heads, causal,
+                               default_sm_scale())
 
 
 def absorbed_inputs(lengths_q, lengths_kv, num_heads: int, seed: int, causal: bool = True,
