@@ -38,8 +38,12 @@
 //  * Software pipeline, one barrier per tile: iteration j publishes tile j+1
 //    (and retires tile j-1), puts tile j+3 in flight into tile j-1's stage,
 //    runs the softmax of tile j, computes the scores of tile j+1, then PV of
-//    tile j, so every wave always has independent MFMA and VALU work to
-//    interleave (softmax first measured slightly faster than scores first).
+//    tile j, and last the max of tile j+1's scores (with the rare O rescale)
+//    while those PV MFMAs run. So after the barrier a wave goes straight from
+//    the DMA issue to MFMAs, and every wave always has independent MFMA and
+//    VALU work to interleave (softmax first measured slightly faster than
+//    scores first; the max at the end of the previous iteration ~6% faster
+//    than at the top of its own).
 //  * Online softmax in base 2 with sm_scale * log2(e) folded into one FMA.
 //    The running max is raised only when a tile's max exceeds it by more
 //    than 2^8 (a stale max keeps every p <= 256 and is exact after the final
@@ -118,6 +122,18 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const vo
                  :: "s"(lds_addr), "v"(voff), "s"(base) : "memory", "m0");
 }
 
+// The same load with M0 = lds_base + OFF set by one scalar add (lds_base
+// and sbase are wave-uniform values already in SGPRs).
+template <int OFF>
+__device__ __forceinline__ void dma16o(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, %3"
+                 :: "s"(lds_base), "n"(OFF), "v"(voff), "s"(base) : "memory", "m0", "scc");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -179,7 +195,7 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     const int last_key = it.kv_len - 1;
     // Per-lane byte offsets (from the tile's first key row) of this wave's
     // loads: 3 K blocks and 2 V blocks; recomputed with the clamp only on a
-    // sequence's last tile.
+    // sequence's last tile. The tile's own address is a scalar base.
     const uint32_t krow = (uint32_t)H * kDqk * 2;
     const uint32_t vrow = (uint32_t)H * kDvo * 2;
     int ld_row[kKBlocksPerWave + kVBlocksPerWave];
@@ -380,10 +396,56 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     if constexpr (kPaged) {
         if (total_tiles > 0) iss_page = page_entry(0);
     }
+    // Contiguous K/V: the cursor's tile addresses advance by one tile of
+    // rows per issue and the stage's LDS address rotates through the ring,
+    // so an issue costs a few scalar adds instead of a 64-bit address
+    // computation (the DMA issue sits between the barrier and the MFMAs).
+    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+    const uint32_t wk_lds = (uint32_t)(wave * kKBlocksPerWave * 1024);
+    const uint32_t wv_lds = (uint32_t)(kKBytes + wave * kVBlocksPerWave * 1024);
+    uint32_t iss_lds = smem_lds;
+    const uint64_t kstep = (uint64_t)kBN * H * (kDqk * 2);
+    const uint64_t vstep = (uint64_t)kBN * H * (kDvo * 2);
+    const uint8_t* iss_kb = kseq + (uint64_t)it.head0 * (kDqk * 2);
+    const uint8_t* iss_vb = vseq + (uint64_t)it.head0 * (kDvo * 2);
     auto issue_next = [&]() {
-        issue_tile(it.head0 + iss_h, iss_kt, iss_g % kStages, iss_page);
+        if constexpr (kPaged) {
+            issue_tile(it.head0 + iss_h, iss_kt, iss_g % kStages, iss_page);
+        } else {
+            static_assert(kKBlocksPerWave == 3 && kVBlocksPerWave == 2, "DMA blocks per wave");
+            const int key0 = iss_kt * kBN;
+            const uint32_t lk = iss_lds + wk_lds, lv = iss_lds + wv_lds;
+            auto issue = [&](const uint32_t (&off)[kKBlocksPerWave + kVBlocksPerWave]) __attribute__((always_inline)) {
+                dma16o<0>(iss_kb, off[0], lk);
+                dma16o<1024>(iss_kb, off[1], lk);
+                dma16o<2048>(iss_kb, off[2], lk);
+                dma16o<0>(iss_vb, off[3], lv);
+                dma16o<1024>(iss_vb, off[4], lv);
+            };
+            if (key0 + kBN - 1 > last_key) {
+                const int lim = last_key - key0;
+                uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
+#pragma unroll
+                for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j) {
+                    const int r = ld_row[j] < lim ? ld_row[j] : lim;
+                    off[j] = (uint32_t)r * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
+                }
+                issue(off);
+            } else {
+                issue(ld_off);
+            }
+        }
         ++iss_g;
-        if (++iss_kt == n_tiles) { iss_kt = 0; ++iss_h; }
+        iss_lds = iss_lds + kStage == smem_lds + kStages * kStage ? smem_lds : iss_lds + kStage;
+        if (++iss_kt == n_tiles) {
+            iss_kt = 0;
+            ++iss_h;
+            iss_kb = kseq + (uint64_t)(it.head0 + iss_h) * (kDqk * 2);
+            iss_vb = vseq + (uint64_t)(it.head0 + iss_h) * (kDvo * 2);
+        } else {
+            iss_kb += kstep;
+            iss_vb += vstep;
+        }
         if constexpr (kPaged) {
             if (iss_g < total_tiles) iss_page = page_entry(iss_kt);
         }
@@ -422,6 +484,23 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
             // and, unless kNext == 0, leaves those of tile j + 1 in s_nxt
             // (kNext: 0 = no next tile, 1 = unmasked, 2 = masked). The loops
             // below alternate two score buffers, so nothing is copied.
+            // The running max for a tile is raised (lazily) before its
+            // softmax: the iteration that computes a tile's scores does it
+            // after its own PV MFMAs are issued, so the max's dependent VALU
+            // chain overlaps them instead of sitting between the next
+            // barrier and the next MFMAs (the O rescale still follows that
+            // PV, the order of the arithmetic is unchanged).
+            auto update_max = [&](const f32x16_t& sv) {
+                const float mt = tile_max(sv);
+                if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
+                    const float m_new = fmaxf(m_run, mt);
+                    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+                }
+            };
             auto iteration = [&](int jj, auto next_kind, const f32x16_t& s_cur, f32x16_t& s_nxt) {
                 constexpr int kNext = decltype(next_kind)::value;
                 const int gt = gbase + jj;
@@ -431,26 +510,19 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
                     // waiting for it later never waits on a younger tile.
                     if (more_heads) load_q(it.head0 + h + 1, qf);
                 }
-                const float mt = tile_max(s_cur);
-                if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
-                    const float m_new = fmaxf(m_run, mt);
-                    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-                    m_run = m_new;
-                    l_run *= alpha;
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-                }
                 bf16x8_t pf[2];
                 softmax(s_cur, pf);
                 if constexpr (kNext == 1) scores(jj + 1, (gt + 1) % kStages, std::false_type{}, s_nxt);
                 if constexpr (kNext == 2) scores(jj + 1, (gt + 1) % kStages, std::true_type{}, s_nxt);
                 pv(gt % kStages, pf);
+                if constexpr (kNext != 0) update_max(s_nxt);
             };
             // The first tile always takes the masked form (a no-op on a fully
             // visible tile): one straight-line path into the loops, on which
             // the compiler sees the Q wait.
             f32x16_t sa, sb;
             scores(0, gbase % kStages, std::true_type{}, sa);
+            update_max(sa);
             // tiles j with an unmasked successor, then with a masked one
             for (; j + 2 < n_full; j += 2) {
                 iteration(j, std::integral_constant<int, 1>{}, sa, sb);
