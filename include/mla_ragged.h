@@ -212,6 +212,16 @@ int mla_plan_info(const mla_plan *plan, int64_t *n_items, int32_t *block_m, int3
                   int32_t *heads_per_item);
 int mla_plan_items(const mla_plan *plan, int32_t *dst, int64_t capacity_items);
 
+/* Work-list entries per workgroup (host only). A bf16 plan of one head per
+ * item pairs two neighbouring light query tiles of a sequence (going up from
+ * its lightest tile, while the keys the two see add up to at most 512) into
+ * one workgroup: if any pair formed, entries 2w and 2w + 1 belong to
+ * workgroup w and run back to back (an entry 2w + 1 with n_rows == 0 is
+ * absent) and this returns 2; otherwise, and for fp32 plans and head blocks,
+ * entry w is workgroup w and it returns 1. The hardware hands workgroup w to
+ * XCD w mod n_xcd. EINVAL on a NULL argument, ESTATE before a plan. */
+int mla_plan_items_per_workgroup(const mla_plan *plan, int32_t *items_per_workgroup);
+
 /* Number of XCDs the partitioner groups work for (default 8, MI355X; 1
  * turns the grouping off). Applies to later mla_ragged_plan calls. */
 int mla_plan_set_xcds(mla_plan *plan, int32_t n_xcd);

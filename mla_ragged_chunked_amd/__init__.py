@@ -37,7 +37,8 @@ _DT = {torch.bfloat16: _BF16, torch.float32: _FP32}
 EXPORTED_SYMBOLS = [
     "mla_status_string", "mla_last_error", "mla_version", "mla_ragged_prefill",
     "mla_plan_create", "mla_plan_destroy", "mla_ragged_plan", "mla_plan_upload",
-    "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_set_xcds",
+    "mla_ragged_run", "mla_plan_info", "mla_plan_items", "mla_plan_items_per_workgroup",
+    "mla_plan_set_xcds",
     "mla_plan_set_heads_per_item", "mla_device_plan_workspace_size",
     "mla_ragged_prefill_device_plan", "mla_ragged_prefill_device_plan_noalloc",
     "mla_ragged_prefill_paged",
@@ -84,6 +85,7 @@ def lib():
         "mla_plan_info": ([P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32),
                            ctypes.POINTER(I32)], ctypes.c_int),
         "mla_plan_items": ([P, P, I64], ctypes.c_int),
+        "mla_plan_items_per_workgroup": ([P, ctypes.POINTER(I32)], ctypes.c_int),
         "mla_plan_set_xcds": ([P, I32], ctypes.c_int),
         "mla_plan_set_heads_per_item": ([P, I32], ctypes.c_int),
         "mla_device_plan_workspace_size": ([I32, I64, I32, I32, ctypes.POINTER(I64)], ctypes.c_int),
@@ -189,8 +191,11 @@ class Plan:
         n, bm, nx, nh = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         _check(self._lib.mla_plan_info(self._h, ctypes.byref(n), ctypes.byref(bm),
                                        ctypes.byref(nx), ctypes.byref(nh)), "mla_plan_info")
+        ipw = ctypes.c_int32()
+        _check(self._lib.mla_plan_items_per_workgroup(self._h, ctypes.byref(ipw)),
+               "mla_plan_items_per_workgroup")
         return {"n_items": n.value, "block_m": bm.value, "n_xcd": nx.value,
-                "heads_per_item": nh.value}
+                "heads_per_item": nh.value, "items_per_workgroup": ipw.value}
 
     def items(self) -> np.ndarray:
         n = self.info()["n_items"]

@@ -200,6 +200,7 @@ struct mla_plan {
     int32_t batch = 0, num_heads = 0, causal = 0, dtype = -1, block_m = 0;
     int32_t n_xcd = 8;
     int32_t heads_per_item = 0;   // 0 = chosen by the planner
+    int32_t items_per_wg = 1;     // work-list entries per workgroup (2: paired tiles)
     bool paged = false;           // items carry the sequence index in kv_start
     bool planned = false;
     bool uploaded = false;
@@ -287,10 +288,14 @@ int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, in
     if (heads < 1) return fail(MLA_EINVAL, "num_heads must be >= 1");
     if (batch > 0 && (qo == nullptr || kv == nullptr)) return fail(MLA_EINVAL, "indptr is NULL");
     const int bm = dtype == MLA_DTYPE_BF16 ? mla::prefill_bf16_block_m() : mla::prefill_fp32_block_m();
+    // the bf16 kernel may run two work-list entries of one head each per
+    // workgroup (paired light tiles); head blocks keep one entry per workgroup
+    const int pair = dtype == MLA_DTYPE_BF16 && p->heads_per_item <= 1 ? mla::kPrefillPairMaxKeys : 0;
+    int per_wg = 1;
     std::string err;
     try {
         if (!mla::build_work_list(qo, kv, batch, heads, causal != 0, bm, p->n_xcd,
-                                  p->heads_per_item, p->items, err, paged))
+                                  p->heads_per_item, p->items, err, paged, pair, &per_wg))
             return fail(MLA_EINVAL, err);
     } catch (const std::bad_alloc&) {
         return fail(MLA_ENOMEM, "host allocation of the work list failed");
@@ -307,6 +312,7 @@ int do_plan(mla_plan* p, const int32_t* qo, const int32_t* kv, int32_t batch, in
     p->causal = causal;
     p->dtype = dtype;
     p->block_m = bm;
+    p->items_per_wg = per_wg;
     p->paged = paged;
     p->planned = true;
     return MLA_OK;
@@ -338,7 +344,7 @@ int do_run(const mla_plan* p, const void* q, const void* k, const void* v, int64
     const int64_t n = static_cast<int64_t>(p->items.size());
     e = dtype == MLA_DTYPE_BF16
             ? mla::launch_prefill_bf16(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale,
-                                       stream, paged)
+                                       stream, paged, p->items_per_wg)
             : mla::launch_prefill_fp32(p->dwl.dev, n, q, k, v, out, lse, p->num_heads, sm_scale,
                                        stream, paged);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
@@ -400,6 +406,7 @@ int oneshot(const void* q, const void* k, const void* v, const int32_t* qo_indpt
     p->causal = causal;
     p->dtype = dtype;
     p->block_m = scratch_check.block_m;
+    p->items_per_wg = scratch_check.items_per_wg;
     p->paged = scratch_check.paged;
     p->planned = true;
     p->uploaded = false;
@@ -767,6 +774,14 @@ int mla_plan_info(const mla_plan* plan, int64_t* n_items, int32_t* block_m, int3
             if (w.n_rows > 0) { nh = w.n_heads; break; }
         *heads_per_item = nh;
     }
+    return MLA_OK;
+}
+
+int mla_plan_items_per_workgroup(const mla_plan* plan, int32_t* items_per_workgroup) {
+    if (plan == nullptr || items_per_workgroup == nullptr)
+        return fail(MLA_EINVAL, "plan or items_per_workgroup is NULL");
+    if (!plan->planned) return fail(MLA_ESTATE, "plan has not been built");
+    *items_per_workgroup = plan->items_per_wg;
     return MLA_OK;
 }
 

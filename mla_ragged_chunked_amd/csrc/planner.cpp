@@ -20,9 +20,19 @@
 //     the XCD bins heaviest first, each to the currently lightest bin (LPT).
 //  4. Each bin lists its groups heaviest first and, inside a group, its
 //     tiles heaviest first, so long tiles start early and the tail is short.
-//  5. The hardware hands workgroup i to XCD i mod n_xcd, so bin x's s-th item
-//     is placed at index s * n_xcd + x; shorter bins are padded with
-//     empty items (n_rows = 0) that the kernel skips.
+//  5. The hardware hands workgroup i to XCD i mod n_xcd, so bin x's s-th
+//     workgroup is placed at slot s * n_xcd + x; shorter bins are padded
+//     with empty items (n_rows = 0) that the kernel skips.
+//  6. Optionally (pair_max_keys > 0) a workgroup runs two items back to
+//     back, the K/V pipeline streaming from the first into the second:
+//     going up from a sequence's lightest tile, two neighbouring tiles are
+//     paired while the keys they see add up to at most pair_max_keys. A
+//     workgroup's fixed cost (Q load, pipeline fill and drain, the
+//     hardware's dispatch of a workgroup) is a large share of such light
+//     tiles and paid once for both; heavy tiles stay alone, so the units
+//     the tail is balanced with stay fine-grained. If any pair forms, the
+//     list holds two entries per workgroup slot (the second one empty for
+//     a lone tile), else one.
 #include <algorithm>
 #include <numeric>
 
@@ -41,12 +51,15 @@ struct Tile {
 
 bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_heads,
                      bool causal, int block_m, int n_xcd, int heads_per_item,
-                     std::vector<WorkItem>& out, std::string& err, bool kv_start_is_seq) {
+                     std::vector<WorkItem>& out, std::string& err, bool kv_start_is_seq,
+                     int pair_max_keys, int* items_per_wg) {
     out.clear();
+    if (items_per_wg != nullptr) *items_per_wg = 1;
     if (batch < 0) { err = "batch must be >= 0"; return false; }
     if (num_heads < 1 || num_heads > 65535) { err = "num_heads must be in [1, 65535]"; return false; }
     if (block_m < 1) { err = "block_m must be >= 1"; return false; }
     if (n_xcd < 1 || n_xcd > 64) { err = "n_xcd must be in [1, 64]"; return false; }
+    if (pair_max_keys < 0) { err = "pair_max_keys must be >= 0"; return false; }
     if (heads_per_item < 0 || (heads_per_item > 0 && num_heads % heads_per_item != 0)) {
         err = "heads_per_item must be 0 (automatic) or divide num_heads";
         return false;
@@ -106,6 +119,36 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
     std::stable_sort(groups.begin(), groups.end(),
                      [](const Group& a, const Group& c) { return a.cost > c.cost; });
 
+    // Workgroup units of every sequence: one tile, or a pair of light tiles
+    // (the lighter one first); heaviest unit first. -1 marks no second tile.
+    struct Unit { int64_t first, second, cost; };
+    std::vector<std::vector<Unit>> seq_units(batch);
+    bool any_pair = false;
+    for (int b = 0; b < batch; ++b) {
+        const size_t begin = seq_tiles[b].first, m = seq_tiles[b].second - begin;
+        std::vector<Unit>& u = seq_units[b];
+        // tiles are sorted heaviest first: walk from the lightest (index m-1)
+        size_t i = m;
+        while (i > 0) {
+            const int64_t t = static_cast<int64_t>(begin + i - 1);
+            if (pair_max_keys > 0 && i >= 2) {
+                const int64_t t2 = t - 1;
+                if (static_cast<int64_t>(tiles[t].kv_hi) + tiles[t2].kv_hi <= pair_max_keys) {
+                    u.push_back({t, t2, tiles[t].cost + tiles[t2].cost});
+                    any_pair = true;
+                    i -= 2;
+                    continue;
+                }
+            }
+            u.push_back({t, -1, tiles[t].cost});
+            i -= 1;
+        }
+        std::stable_sort(u.begin(), u.end(),
+                         [](const Unit& a, const Unit& c) { return a.cost > c.cost; });
+    }
+    const size_t per_wg = any_pair ? 2 : 1;
+    if (items_per_wg != nullptr) *items_per_wg = static_cast<int>(per_wg);
+
     // LPT deal into XCD bins.
     std::vector<std::vector<const Group*>> bins(n_xcd);
     std::vector<int64_t> load(n_xcd, 0);
@@ -116,26 +159,31 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
             if (load[x] < load[best]) best = x;
         bins[best].push_back(&g);
         load[best] += g.cost;
-        count[best] += seq_tiles[g.seq].second - seq_tiles[g.seq].first;
+        count[best] += seq_units[g.seq].size();
     }
     const size_t slots = *std::max_element(count.begin(), count.end());
 
     WorkItem pad{};
-    out.assign(slots * static_cast<size_t>(n_xcd), pad);
+    out.assign(slots * static_cast<size_t>(n_xcd) * per_wg, pad);
+    auto put = [&](size_t at, const Tile& t, int32_t head0) {
+        WorkItem& w = out[at];
+        w.q_row0 = t.q_row0;
+        w.n_rows = t.n_rows;
+        w.head0 = head0;
+        w.n_heads = nh;
+        w.kv_start = t.kv_start;
+        w.kv_len = t.kv_len;
+        w.diag0 = t.diag0;
+        w.kv_hi = t.kv_hi;
+    };
     for (int x = 0; x < n_xcd; ++x) {
         size_t s = 0;
         for (const Group* g : bins[x]) {
-            for (size_t i = seq_tiles[g->seq].first; i < seq_tiles[g->seq].second; ++i, ++s) {
-                const Tile& t = tiles[i];
-                WorkItem& w = out[s * n_xcd + x];
-                w.q_row0 = t.q_row0;
-                w.n_rows = t.n_rows;
-                w.head0 = g->head0;
-                w.n_heads = nh;
-                w.kv_start = t.kv_start;
-                w.kv_len = t.kv_len;
-                w.diag0 = t.diag0;
-                w.kv_hi = t.kv_hi;
+            for (const Unit& u : seq_units[g->seq]) {
+                const size_t at = (s * n_xcd + x) * per_wg;
+                put(at, tiles[u.first], g->head0);
+                if (u.second >= 0) put(at + 1, tiles[u.second], g->head0);
+                ++s;
             }
         }
     }

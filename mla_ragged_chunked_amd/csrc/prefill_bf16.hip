@@ -34,7 +34,10 @@
 //    item (recomputed with a clamp only on a sequence's last tile). The ring
 //    runs on from one head of the item into the next without draining, and
 //    the next head's Q is loaded during the current head's last tile, so the
-//    start-up latency is paid once per item rather than once per head.
+//    start-up latency is paid once per item rather than once per head. A
+//    workgroup may also run two items (two light query tiles of one head,
+//    paired by the planner) the same way, the ring streaming from the first
+//    into the second.
 //  * Software pipeline, one barrier per tile: iteration j publishes tile j+1
 //    (and retires tile j-1), puts tile j+3 in flight into tile j-1's stage,
 //    runs the softmax of tile j, computes the scores of tile j+1, then PV of
@@ -126,12 +129,13 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const vo
 // and sbase are wave-uniform values already in SGPRs).
 template <int OFF>
 __device__ __forceinline__ void dma16o(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
     const uint64_t b = (uint64_t)(uintptr_t)sbase;
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
     const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
     asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, %3"
-                 :: "s"(lds_base), "n"(OFF), "v"(voff), "s"(base) : "memory", "m0", "scc");
+                 :: "s"(lds), "n"(OFF), "v"(voff), "s"(base) : "memory", "m0", "scc");
 }
 
 template <int N>
@@ -140,17 +144,28 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <bool kPaged>
+// kPair: two work-list entries per workgroup, each of one head (the paired
+// layout of the planner); otherwise one entry of n_heads heads.
+template <bool kPaged, bool kPair>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
-                         const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                         uint16_t* __restrict__ out, float* __restrict__ lse, int num_heads,
-                         float scale_log2, PagedKv pg,
+void prefill_bf16_kernel(const WorkItem* __restrict__ items,
+                         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                         const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
+                         float* __restrict__ lse, int num_heads, float scale_log2, PagedKv pg,
                          const int32_t* __restrict__ block_table) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
-    const WorkItem it = items[blockIdx.x];
-    if (it.n_rows <= 0) return;
+    // This workgroup's items: one, or two run back to back (a second item
+    // with n_rows == 0 is absent). A unit is one head of one item; the
+    // units run in order (item 0's heads, then item 1's) with the K/V ring
+    // streaming from one into the next.
+    const WorkItem* wi = items + (int64_t)blockIdx.x * (kPair ? 2 : 1);
+    const WorkItem it0 = wi[0];
+    if (it0.n_rows <= 0) return;
+    const WorkItem it1 = kPair ? wi[1] : it0;
+    const int n_it = kPair && it1.n_rows > 0 ? 2 : 1;
+    // heads of an item (paired entries hold one head each)
+    auto heads_of = [&](const WorkItem& w) { return kPair ? 1 : w.n_heads; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -159,22 +174,20 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     const int g = lane >> 5;
     const int H = num_heads;
     const int row_w0 = wave * 32;
-    int wave_rows = it.n_rows - row_w0;
-    wave_rows = wave_rows < 0 ? 0 : (wave_rows > 32 ? 32 : wave_rows);
-    const int wave_lo = wave_rows > 0 ? lim_of(row_w0, it.diag0, it.kv_len) : 0;
-    const int wave_hi = wave_rows > 0 ? lim_of(row_w0 + wave_rows - 1, it.diag0, it.kv_len) : 0;
-
-    // Q fragments (B operand): row row_w0 + l32, dims 16*s + 8*g .. +8
-    bf16x8_t qf[kKSteps];
     const int my_row = row_w0 + l32;
-    const int my_lim = lim_of(my_row, it.diag0, it.kv_len);
-    // Rows past the tile's end load its last row instead (their results
-    // are never stored), so every lane loads and no lane needs zero-filling.
-    const int q_row = it.q_row0 + (my_row < it.n_rows ? my_row : it.n_rows - 1);
-    auto load_q = [&](int head, bf16x8_t (&dst)[kKSteps]) {
+    auto tiles_of = [&](const WorkItem& w) { return (w.kv_hi + kBN - 1) / kBN; };
+    const int nt0 = tiles_of(it0);
+    const int total_tiles = nt0 * heads_of(it0) + (n_it > 1 ? tiles_of(it1) : 0);
+
+    // Q fragments (B operand): row row_w0 + l32, dims 16*s + 8*g .. +8.
+    // Rows past the tile's end load its last row instead (their results are
+    // never stored), so every lane loads and no lane needs zero-filling.
+    bf16x8_t qf[kKSteps];
+    auto load_q = [&](const WorkItem& w, int head) {
+        const int q_row = w.q_row0 + (my_row < w.n_rows ? my_row : w.n_rows - 1);
         const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(q + ((int64_t)q_row * H + head) * kDqk);
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) dst[s] = src[s * 2 + g];
+        for (int s = 0; s < kKSteps; ++s) qf[s] = src[s * 2 + g];
     };
 
     f32x16_t oacc[4];
@@ -189,75 +202,129 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     // V: 8 blocks of 4 rows x 256 B; row r's chunk c sits at slot vslot(r, c).
     // Keys at or past kv_len load the last valid row instead (finite data;
     // the mask gives those keys p = 0).
-    // row index of key 0, head 0 (contiguous K/V; paged K/V address each tile
-    // through its page)
-    const int64_t kv_row0 = kPaged ? 0 : (int64_t)it.kv_start * H;
-    const int last_key = it.kv_len - 1;
     // Per-lane byte offsets (from the tile's first key row) of this wave's
     // loads: 3 K blocks and 2 V blocks; recomputed with the clamp only on a
     // sequence's last tile. The tile's own address is a scalar base.
     const uint32_t krow = (uint32_t)H * kDqk * 2;
     const uint32_t vrow = (uint32_t)H * kDvo * 2;
-    int ld_row[kKBlocksPerWave + kVBlocksPerWave];
-    uint32_t ld_col[kKBlocksPerWave + kVBlocksPerWave];
-#pragma unroll
-    for (int j = 0; j < kKBlocksPerWave; ++j) {
-        // block bi = 3 R + G: rows 8R .. 8R+7, 16-byte chunks 8G .. 8G+7 of
-        // each row (128 contiguous bytes per row), chunk order XOR-swizzled
-        const int bi = wave * kKBlocksPerWave + j;
-        ld_row[j] = (bi / 3) * 8 + (lane >> 3);
-        ld_col[j] = ((bi % 3) * 8 + ((lane & 7) ^ ((ld_row[j] >> 1) & 7))) * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < kVBlocksPerWave; ++j) {
-        const int b = wave * kVBlocksPerWave + j;
-        ld_row[kKBlocksPerWave + j] = 4 * b + (lane >> 4);
-        ld_col[kKBlocksPerWave + j] = vslot(ld_row[kKBlocksPerWave + j], lane & 15) * 16;
-    }
+    // row (key within the tile) and byte column of load j of this lane; the
+    // clamped form is only needed on a sequence's last tile, so row and
+    // column are recomputed there rather than kept in registers
+    auto ld_row = [&](int j) {
+        if (j < kKBlocksPerWave) {
+            // block bi = 3 R + G: rows 8R .. 8R+7, 16-byte chunks 8G .. 8G+7
+            // of each row (128 contiguous bytes per row), chunk order XOR-swizzled
+            const int bi = wave * kKBlocksPerWave + j;
+            return (bi / 3) * 8 + (lane >> 3);
+        }
+        return 4 * (wave * kVBlocksPerWave + j - kKBlocksPerWave) + (lane >> 4);
+    };
+    auto ld_col = [&](int j) {
+        const int row = ld_row(j);
+        if (j < kKBlocksPerWave)
+            return (uint32_t)((((wave * kKBlocksPerWave + j) % 3) * 8 + ((lane & 7) ^ ((row >> 1) & 7))) * 16);
+        return (uint32_t)(vslot(row, lane & 15) * 16);
+    };
     uint32_t ld_off[kKBlocksPerWave + kVBlocksPerWave];
 #pragma unroll
     for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j)
-        ld_off[j] = (uint32_t)ld_row[j] * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
-    const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k + kv_row0 * kDqk);
-    const uint8_t* vseq = reinterpret_cast<const uint8_t*>(v + kv_row0 * kDvo);
-    // Table entry of key tile kt (paged K/V). The block table is a kernel
-    // argument of its own, __restrict__, so this is a scalar load, which does
-    // not count against the DMA waits; the raw value is clamped only where it
-    // is used, an issue later, so the load's latency is never waited for.
-    auto page_entry = [&](int kt) {
-        return block_table[(int64_t)it.kv_start * pg.max_pages + (kt * kBN) / pg.page_size];
+        ld_off[j] = (uint32_t)ld_row(j) * (j < kKBlocksPerWave ? krow : vrow) + ld_col(j);
+    const uint8_t* k8 = reinterpret_cast<const uint8_t*>(k);
+    const uint8_t* v8 = reinterpret_cast<const uint8_t*>(v);
+
+    // ---- issue cursor: the next tile to put in flight ----
+    // Contiguous K/V: the cursor's tile addresses advance by one tile of
+    // rows per issue and the stage's LDS address rotates through the ring,
+    // so an issue costs a few scalar adds (the issue sits between the
+    // barrier and the MFMAs). Paged K/V address every tile through its page;
+    // the block table is a kernel argument of its own, __restrict__, so its
+    // entries are scalar loads (they do not count against the DMA waits),
+    // read one issue ahead and clamped only where used.
+    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+    const uint32_t wk_lds = (uint32_t)(wave * kKBlocksPerWave * 1024);
+    const uint32_t wv_lds = (uint32_t)(kKBytes + wave * kVBlocksPerWave * 1024);
+    const uint64_t kstep = (uint64_t)kBN * H * (kDqk * 2);
+    const uint64_t vstep = (uint64_t)kBN * H * (kDvo * 2);
+    uint32_t iss_lds = smem_lds;
+    int iss_g = 0, iss_u = 0, iss_h = 0, iss_kt = 0;
+    int iss_nt = 0, iss_nh = 0, iss_head0 = 0, iss_seq = 0, iss_last = -1;
+    int64_t iss_row0 = 0;    // row of key 0 of the cursor's item (contiguous K/V)
+    const uint8_t* iss_kb = k8;
+    const uint8_t* iss_vb = v8;
+    // point the cursor at key tile 0 of the first head of item w
+    auto iss_enter = [&](const WorkItem& w) {
+        iss_nt = tiles_of(w);
+        iss_nh = heads_of(w);
+        iss_head0 = w.head0;
+        iss_seq = w.kv_start;
+        iss_last = w.kv_len - 1;
+        iss_row0 = kPaged ? 0 : (int64_t)w.kv_start * H;
+        iss_kb = k8 + (iss_row0 + iss_head0) * (kDqk * 2);
+        iss_vb = v8 + (iss_row0 + iss_head0) * (kDvo * 2);
     };
-    // Tile kt of head `head` into `stage` (`entry`: its table entry, paged K/V only).
-    auto issue_tile = [&](int head, int kt, int stage, int entry) {
-        uint8_t* ks = smem + stage * kStage;
-        uint8_t* vs = ks + kKBytes;
-        const int key0 = kt * kBN;
-        uint64_t row0 = (uint64_t)key0;
+    // an item without key tiles (its rows see no key) has nothing to load
+    iss_enter(it0);
+    if (iss_nt == 0 && n_it > 1) {
+        iss_u = 1;
+        iss_enter(it1);
+    }
+    auto page_entry = [&](int kt) {
+        return block_table[(int64_t)iss_seq * pg.max_pages + (kt * kBN) / pg.page_size];
+    };
+    int iss_page = 0;
+    if constexpr (kPaged) {
+        if (total_tiles > 0) iss_page = page_entry(0);
+    }
+    auto issue_next = [&]() {
+        const int key0 = iss_kt * kBN;
+        const uint8_t* kb = iss_kb;
+        const uint8_t* vb = iss_vb;
         if constexpr (kPaged) {
-            const int page = entry < 0 ? 0 : (entry >= pg.num_pages ? pg.num_pages - 1 : entry);
-            row0 = (uint64_t)page * pg.page_size + (uint64_t)(key0 % pg.page_size);
+            const int page = iss_page < 0 ? 0 : (iss_page >= pg.num_pages ? pg.num_pages - 1 : iss_page);
+            const uint64_t row0 = (uint64_t)page * pg.page_size + (uint64_t)(key0 % pg.page_size);
+            kb = k8 + (row0 * H + iss_head0 + iss_h) * (kDqk * 2);
+            vb = v8 + (row0 * H + iss_head0 + iss_h) * (kDvo * 2);
         }
-        const uint8_t* kb = kseq + (row0 * H + head) * (kDqk * 2);
-        const uint8_t* vb = vseq + (row0 * H + head) * (kDvo * 2);
+        static_assert(kKBlocksPerWave == 3 && kVBlocksPerWave == 2, "DMA blocks per wave");
+        const uint32_t lk = iss_lds + wk_lds, lv = iss_lds + wv_lds;
         auto issue = [&](const uint32_t (&off)[kKBlocksPerWave + kVBlocksPerWave]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < kKBlocksPerWave; ++j)
-                dma16(kb, off[j], ks + (wave * kKBlocksPerWave + j) * 1024);
-#pragma unroll
-            for (int j = 0; j < kVBlocksPerWave; ++j)
-                dma16(vb, off[kKBlocksPerWave + j], vs + (wave * kVBlocksPerWave + j) * 1024);
+            dma16o<0>(kb, off[0], lk);
+            dma16o<1024>(kb, off[1], lk);
+            dma16o<2048>(kb, off[2], lk);
+            dma16o<0>(vb, off[3], lv);
+            dma16o<1024>(vb, off[4], lv);
         };
-        if (key0 + kBN - 1 > last_key) {
-            const int lim = last_key - key0;
+        if (key0 + kBN - 1 > iss_last) {
+            const int lim = iss_last - key0;
             uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
 #pragma unroll
             for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j) {
-                const int r = ld_row[j] < lim ? ld_row[j] : lim;
-                off[j] = (uint32_t)r * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
+                const int r = ld_row(j) < lim ? ld_row(j) : lim;
+                off[j] = (uint32_t)r * (j < kKBlocksPerWave ? krow : vrow) + ld_col(j);
             }
             issue(off);
         } else {
             issue(ld_off);
+        }
+        ++iss_g;
+        iss_lds = iss_lds + kStage == smem_lds + kStages * kStage ? smem_lds : iss_lds + kStage;
+        if (++iss_kt == iss_nt) {
+            iss_kt = 0;
+            if (++iss_h == iss_nh) {
+                // the next item (the cursor only gets here while tiles remain,
+                // so that item has key tiles)
+                iss_h = 0;
+                if (++iss_u < n_it) iss_enter(it1);
+            } else {
+                iss_kb = k8 + (iss_row0 + iss_head0 + iss_h) * (kDqk * 2);
+                iss_vb = v8 + (iss_row0 + iss_head0 + iss_h) * (kDvo * 2);
+            }
+        } else if constexpr (!kPaged) {
+            iss_kb += kstep;
+            iss_vb += vstep;
+        }
+        if constexpr (kPaged) {
+            if (iss_g < total_tiles) iss_page = page_entry(iss_kt);
         }
     };
 
@@ -269,6 +336,7 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         k_off[t] = (l32 >> 3) * 3 * 1024 + ((l32 & 7) * 8 + ((2 * t + g) ^ ((l32 >> 1) & 7))) * 16;
 
     // ---- compute pieces ----
+    int my_lim = 0;    // keys visible to this lane's row in the current item
     auto scores = [&](int kt, int stage, auto masked, f32x16_t& sacc) {
         constexpr bool kMasked = decltype(masked)::value;
         const uint8_t* ks = smem + stage * kStage;
@@ -356,13 +424,14 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         }
     };
 
-    // O = acc / l and LSE = (m + log2 l) ln 2 for head `head` (waves with rows)
-    auto store_out = [&](int head) {
-        if (wave_rows <= 0) return;
+    // O = acc / l and LSE = (m + log2 l) ln 2 for one head of item w
+    // (waves with rows in it)
+    auto store_out = [&](const WorkItem& w, int head) {
+        if (w.n_rows - row_w0 <= 0) return;
         const float ltot = xor32_sum(l_run);
-        if (my_row >= it.n_rows) return;
+        if (my_row >= w.n_rows) return;
         const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
-        const int64_t orow = (int64_t)(it.q_row0 + my_row) * H + head;
+        const int64_t orow = (int64_t)(w.q_row0 + my_row) * H + head;
         uint16_t* dst = out + orow * kDvo;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
@@ -379,81 +448,11 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
             lse[orow] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
     };
 
-    // Tiles per head; the item's heads run one after the other and the K/V
-    // ring streams on across head boundaries: global tile g = h * n_tiles + kt
-    // (h = head index in the block) lives in stage g % kStages.
-    const int n_tiles = (it.kv_hi + kBN - 1) / kBN;
-    const int n_heads = it.n_heads;
-    const int total_tiles = n_tiles * n_heads;
-    const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
-    const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
-
-    // issue cursor: the next global tile to put in flight; with paged K/V
-    // the page of that tile is read one issue ahead, so the table lookup's
-    // latency is hidden behind an iteration
-    int iss_g = 0, iss_h = 0, iss_kt = 0;
-    int iss_page = 0;
-    if constexpr (kPaged) {
-        if (total_tiles > 0) iss_page = page_entry(0);
-    }
-    // Contiguous K/V: the cursor's tile addresses advance by one tile of
-    // rows per issue and the stage's LDS address rotates through the ring,
-    // so an issue costs a few scalar adds instead of a 64-bit address
-    // computation (the DMA issue sits between the barrier and the MFMAs).
-    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-    const uint32_t wk_lds = (uint32_t)(wave * kKBlocksPerWave * 1024);
-    const uint32_t wv_lds = (uint32_t)(kKBytes + wave * kVBlocksPerWave * 1024);
-    uint32_t iss_lds = smem_lds;
-    const uint64_t kstep = (uint64_t)kBN * H * (kDqk * 2);
-    const uint64_t vstep = (uint64_t)kBN * H * (kDvo * 2);
-    const uint8_t* iss_kb = kseq + (uint64_t)it.head0 * (kDqk * 2);
-    const uint8_t* iss_vb = vseq + (uint64_t)it.head0 * (kDvo * 2);
-    auto issue_next = [&]() {
-        if constexpr (kPaged) {
-            issue_tile(it.head0 + iss_h, iss_kt, iss_g % kStages, iss_page);
-        } else {
-            static_assert(kKBlocksPerWave == 3 && kVBlocksPerWave == 2, "DMA blocks per wave");
-            const int key0 = iss_kt * kBN;
-            const uint32_t lk = iss_lds + wk_lds, lv = iss_lds + wv_lds;
-            auto issue = [&](const uint32_t (&off)[kKBlocksPerWave + kVBlocksPerWave]) __attribute__((always_inline)) {
-                dma16o<0>(iss_kb, off[0], lk);
-                dma16o<1024>(iss_kb, off[1], lk);
-                dma16o<2048>(iss_kb, off[2], lk);
-                dma16o<0>(iss_vb, off[3], lv);
-                dma16o<1024>(iss_vb, off[4], lv);
-            };
-            if (key0 + kBN - 1 > last_key) {
-                const int lim = last_key - key0;
-                uint32_t off[kKBlocksPerWave + kVBlocksPerWave];
-#pragma unroll
-                for (int j = 0; j < kKBlocksPerWave + kVBlocksPerWave; ++j) {
-                    const int r = ld_row[j] < lim ? ld_row[j] : lim;
-                    off[j] = (uint32_t)r * (j < kKBlocksPerWave ? krow : vrow) + ld_col[j];
-                }
-                issue(off);
-            } else {
-                issue(ld_off);
-            }
-        }
-        ++iss_g;
-        iss_lds = iss_lds + kStage == smem_lds + kStages * kStage ? smem_lds : iss_lds + kStage;
-        if (++iss_kt == n_tiles) {
-            iss_kt = 0;
-            ++iss_h;
-            iss_kb = kseq + (uint64_t)(it.head0 + iss_h) * (kDqk * 2);
-            iss_vb = vseq + (uint64_t)(it.head0 + iss_h) * (kDvo * 2);
-        } else {
-            iss_kb += kstep;
-            iss_vb += vstep;
-        }
-        if constexpr (kPaged) {
-            if (iss_g < total_tiles) iss_page = page_entry(iss_kt);
-        }
-    };
-    // Software pipeline: the iteration for global tile g publishes tile g+1
-    // (one barrier; it also retires tile g-1), puts tile g+3 in flight into
-    // tile g-1's stage, computes the scores of the next tile of the same head
-    // and runs softmax + PV of tile g.
+    // Software pipeline over the global tile index gt (all units' tiles in
+    // order; tile gt lives in stage gt % kStages): the iteration for tile
+    // gt publishes tile gt+1 (one barrier, which also retires tile gt-1),
+    // puts tile gt+3 in flight into tile gt-1's stage, computes the scores
+    // of the unit's next tile and runs softmax + PV of tile gt.
     auto sync_top = [&](int gt) {
         // loads issued so far: tiles 0 .. gt+2; tile gt+1 must be complete
         if (gt + 2 < total_tiles) wait_vmcnt<kLoadsPerTile>();
@@ -462,8 +461,15 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
         if (gt + 3 < total_tiles) issue_next();
     };
 
-    // A wave whose rows see no key never reads Q.
-    if (n_wave > 0) load_q(it.head0, qf);
+    // A wave whose rows see no key of the first unit does not read its Q
+    // (it loads the Q of its first unit with work when it gets there).
+    auto wave_hi_of = [&](const WorkItem& w) {
+        int wr = w.n_rows - row_w0;
+        wr = wr < 0 ? 0 : (wr > 32 ? 32 : wr);
+        return wr > 0 ? lim_of(row_w0 + wr - 1, w.diag0, w.kv_len) : 0;
+    };
+    bool q_ready = wave_hi_of(it0) > 0;     // qf holds the Q of the next unit with work
+    if (q_ready) load_q(it0, it0.head0);
     for (int t = 0; t < 3 && t < total_tiles; ++t) issue_next();
     // Q and tile 0 must be complete: tiles 1 and 2 may still be in flight
     if (total_tiles > 2) wait_vmcnt<2 * kLoadsPerTile>();
@@ -471,92 +477,130 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items, const uint16_t* __r
     else wait_vmcnt<0>();
     __syncthreads();
 
-    for (int h = 0; h < n_heads; ++h) {
-        const int gbase = h * n_tiles;
-        const bool more_heads = h + 1 < n_heads;
-        int j = 0;
-        if (n_wave > 0) {
+    int gbase = 0;
+    for (int u = 0; u < n_it; ++u) {
+        const WorkItem w = u == 0 ? it0 : it1;
+        const int n_tiles = tiles_of(w);
+        int wave_rows = w.n_rows - row_w0;
+        wave_rows = wave_rows < 0 ? 0 : (wave_rows > 32 ? 32 : wave_rows);
+        const int wave_lo = wave_rows > 0 ? lim_of(row_w0, w.diag0, w.kv_len) : 0;
+        const int wave_hi = wave_rows > 0 ? lim_of(row_w0 + wave_rows - 1, w.diag0, w.kv_len) : 0;
+        my_lim = lim_of(my_row, w.diag0, w.kv_len);
+        const int n_full = __builtin_amdgcn_readfirstlane(wave_lo / kBN);
+        const int n_wave = __builtin_amdgcn_readfirstlane((wave_hi + kBN - 1) / kBN);
+        for (int h = 0; h < heads_of(w); ++h, gbase += n_tiles) {
+            // the unit after this one, if any, and whether this wave has work there
+            const bool next_same = h + 1 < heads_of(w);
+            const bool has_next = next_same || u + 1 < n_it;
+            const WorkItem wn = next_same || u + 1 >= n_it ? w : it1;
+            const int head_next = next_same ? w.head0 + h + 1 : wn.head0;
+            const bool next_work = has_next && (next_same ? n_wave > 0 : wave_hi_of(wn) > 0);
+            int j = 0;
+            bool loaded_next = false;
+            if (n_wave > 0) {
+                if (!q_ready) {
+                    // no Q was loaded for this unit: load it and wait (this
+                    // also waits for the ring's loads in flight)
+                    load_q(w, w.head0 + h);
+                    __builtin_amdgcn_s_waitcnt(kVmcnt0);
 #pragma unroll
-            for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
-            m_run = -INFINITY;
-            l_run = 0.f;
-            // One pipelined iteration: consumes the scores of tile j in s_cur
-            // and, unless kNext == 0, leaves those of tile j + 1 in s_nxt
-            // (kNext: 0 = no next tile, 1 = unmasked, 2 = masked). The loops
-            // below alternate two score buffers, so nothing is copied.
-            // The running max for a tile is raised (lazily) before its
-            // softmax: the iteration that computes a tile's scores does it
-            // after its own PV MFMAs are issued, so the max's dependent VALU
-            // chain overlaps them instead of sitting between the next
-            // barrier and the next MFMAs (the O rescale still follows that
-            // PV, the order of the arithmetic is unchanged).
-            auto update_max = [&](const f32x16_t& sv) {
-                const float mt = tile_max(sv);
-                if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
-                    const float m_new = fmaxf(m_run, mt);
-                    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-                    m_run = m_new;
-                    l_run *= alpha;
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+                    for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+v"(qf[s]));
                 }
-            };
-            auto iteration = [&](int jj, auto next_kind, const f32x16_t& s_cur, f32x16_t& s_nxt) {
-                constexpr int kNext = decltype(next_kind)::value;
-                const int gt = gbase + jj;
-                sync_top(gt);
-                if constexpr (kNext == 0) {
-                    // The next head's Q: issued after this tile's DMA, so
-                    // waiting for it later never waits on a younger tile.
-                    if (more_heads) load_q(it.head0 + h + 1, qf);
-                }
-                bf16x8_t pf[2];
-                softmax(s_cur, pf);
-                if constexpr (kNext == 1) scores(jj + 1, (gt + 1) % kStages, std::false_type{}, s_nxt);
-                if constexpr (kNext == 2) scores(jj + 1, (gt + 1) % kStages, std::true_type{}, s_nxt);
-                pv(gt % kStages, pf);
-                if constexpr (kNext != 0) update_max(s_nxt);
-            };
-            // The first tile always takes the masked form (a no-op on a fully
-            // visible tile): one straight-line path into the loops, on which
-            // the compiler sees the Q wait.
-            f32x16_t sa, sb;
-            scores(0, gbase % kStages, std::true_type{}, sa);
-            update_max(sa);
-            // tiles j with an unmasked successor, then with a masked one
-            for (; j + 2 < n_full; j += 2) {
-                iteration(j, std::integral_constant<int, 1>{}, sa, sb);
-                iteration(j + 1, std::integral_constant<int, 1>{}, sb, sa);
-            }
-            if (j + 1 < n_full) {
-                iteration(j, std::integral_constant<int, 1>{}, sa, sb);
-                sa = sb;
-                ++j;
-            }
-            for (; j + 2 < n_wave; j += 2) {
-                iteration(j, std::integral_constant<int, 2>{}, sa, sb);
-                iteration(j + 1, std::integral_constant<int, 2>{}, sb, sa);
-            }
-            if (j + 1 < n_wave) {
-                iteration(j, std::integral_constant<int, 2>{}, sa, sb);
-                sa = sb;
-                ++j;
-            }
-            iteration(j, std::integral_constant<int, 0>{}, sa, sb);
-            ++j;
-            // The next head's Q loads are the youngest vector-memory reads:
-            // completing them here costs no ring tile. The empty asm then
-            // redefines the Q registers, so the compiler no longer sees loads
-            // in flight into them and puts no waits of its own in the loops.
-            if (more_heads) {
-                __builtin_amdgcn_s_waitcnt(kVmcnt0);
 #pragma unroll
-                for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+v"(qf[s]));
+                for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+                m_run = -INFINITY;
+                l_run = 0.f;
+                // The running max for a tile is raised (lazily) before its
+                // softmax: the iteration that computes a tile's scores does
+                // it after its own PV MFMAs are issued, so the max's
+                // dependent VALU chain overlaps them instead of sitting
+                // between the next barrier and the next MFMAs (the O rescale
+                // still follows that PV, the order of the arithmetic is
+                // unchanged).
+                auto update_max = [&](const f32x16_t& sv) {
+                    const float mt = tile_max(sv);
+                    if (__builtin_expect(__any(mt > m_run + kLazyRescale), 0)) {
+                        const float m_new = fmaxf(m_run, mt);
+                        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+                        m_run = m_new;
+                        l_run *= alpha;
+#pragma unroll
+                        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+                    }
+                };
+                // One pipelined iteration: consumes the scores of tile j in
+                // s_cur and, unless kNext == 0, leaves those of tile j + 1 in
+                // s_nxt (kNext: 0 = no next tile, 1 = unmasked, 2 = masked).
+                // The loops below alternate two score buffers, so nothing is
+                // copied.
+                auto iteration = [&](int jj, auto next_kind, const f32x16_t& s_cur, f32x16_t& s_nxt) {
+                    constexpr int kNext = decltype(next_kind)::value;
+                    const int gt = gbase + jj;
+                    sync_top(gt);
+                    if constexpr (kNext == 0) {
+                        // The next unit's Q: issued after this tile's DMA, so
+                        // waiting for it later never waits on a younger tile.
+                        if (next_work) {
+                            load_q(wn, head_next);
+                            loaded_next = true;
+                        }
+                    }
+                    bf16x8_t pf[2];
+                    softmax(s_cur, pf);
+                    if constexpr (kNext == 1) scores(jj + 1, (gt + 1) % kStages, std::false_type{}, s_nxt);
+                    if constexpr (kNext == 2) scores(jj + 1, (gt + 1) % kStages, std::true_type{}, s_nxt);
+                    pv(gt % kStages, pf);
+                    if constexpr (kNext != 0) update_max(s_nxt);
+                };
+                // The first tile always takes the masked form (a no-op on a
+                // fully visible tile): one straight-line path into the loops,
+                // on which the compiler sees the Q wait.
+                f32x16_t sa, sb;
+                scores(0, gbase % kStages, std::true_type{}, sa);
+                update_max(sa);
+                // tiles j with an unmasked successor, then with a masked one
+                for (; j + 2 < n_full; j += 2) {
+                    iteration(j, std::integral_constant<int, 1>{}, sa, sb);
+                    iteration(j + 1, std::integral_constant<int, 1>{}, sb, sa);
+                }
+                if (j + 1 < n_full) {
+                    iteration(j, std::integral_constant<int, 1>{}, sa, sb);
+                    sa = sb;
+                    ++j;
+                }
+                for (; j + 2 < n_wave; j += 2) {
+                    iteration(j, std::integral_constant<int, 2>{}, sa, sb);
+                    iteration(j + 1, std::integral_constant<int, 2>{}, sb, sa);
+                }
+                if (j + 1 < n_wave) {
+                    iteration(j, std::integral_constant<int, 2>{}, sa, sb);
+                    sa = sb;
+                    ++j;
+                }
+                iteration(j, std::integral_constant<int, 0>{}, sa, sb);
+                ++j;
+                // The next unit's Q loads are the youngest vector-memory
+                // reads: completing them here costs no ring tile. The empty
+                // asm then redefines the Q registers, so the compiler no
+                // longer sees loads in flight into them and puts no waits of
+                // its own in the loops.
+                if (loaded_next) {
+                    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+#pragma unroll
+                    for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+v"(qf[s]));
+                }
+            } else {
+                // no row of this wave sees a key of this unit: O = 0, LSE = -inf
+#pragma unroll
+                for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+                m_run = -INFINITY;
+                l_run = 0.f;
             }
+            store_out(w, w.head0 + h);
+            q_ready = loaded_next;
+            // tiles only other waves need: barriers and loads
+            for (; j < n_tiles; ++j) sync_top(gbase + j);
         }
-        store_out(it.head0 + h);
-        // tiles only other waves need: barriers and loads
-        for (; j < n_tiles; ++j) sync_top(gbase + j);
     }
     wait_vmcnt<0>();
 }
@@ -568,23 +612,27 @@ int prefill_bf16_block_m() { return kBM; }
 hipError_t launch_prefill_bf16(const WorkItem* items, int64_t n_items, const void* q,
                                const void* k, const void* v, void* out, float* lse,
                                int num_heads, float sm_scale, hipStream_t stream,
-                               const PagedKv* paged) {
+                               const PagedKv* paged, int items_per_wg) {
     if (n_items <= 0) return hipSuccess;
-    if (n_items > 0x7fffffff) return hipErrorInvalidValue;
+    if (items_per_wg < 1 || items_per_wg > 2 || n_items % items_per_wg != 0)
+        return hipErrorInvalidValue;
+    const int64_t blocks = n_items / items_per_wg;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     const PagedKv pg = paged != nullptr ? *paged : PagedKv{nullptr, 0, 0, 0};
+    const int32_t* table = paged != nullptr ? pg.block_table : nullptr;
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, items,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse,
+                           num_heads, scale_log2, pg, table);
+    };
     if (paged != nullptr)
-        hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)n_items), dim3(kThreads), 0,
-                           stream, items, static_cast<const uint16_t*>(q),
-                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                           static_cast<uint16_t*>(out), lse, num_heads, scale_log2, pg,
-                           pg.block_table);
+        items_per_wg == 2 ? launch(prefill_bf16_kernel<true, true>)
+                          : launch(prefill_bf16_kernel<true, false>);
     else
-        hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)n_items), dim3(kThreads), 0,
-                           stream, items, static_cast<const uint16_t*>(q),
-                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                           static_cast<uint16_t*>(out), lse, num_heads, scale_log2, pg,
-                           nullptr);
+        items_per_wg == 2 ? launch(prefill_bf16_kernel<false, true>)
+                          : launch(prefill_bf16_kernel<false, false>);
     return hipGetLastError();
 }
 

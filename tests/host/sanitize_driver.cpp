@@ -18,7 +18,7 @@ int prefill_bf16_block_m() { return 128; }
 int prefill_fp32_block_m() { return 64; }
 int prefill_absorbed_block_m() { return 128; }
 hipError_t launch_prefill_bf16(const WorkItem*, int64_t, const void*, const void*, const void*,
-                               void*, float*, int, float, hipStream_t, const PagedKv*) {
+                               void*, float*, int, float, hipStream_t, const PagedKv*, int) {
     return hipErrorInvalidValue;
 }
 hipError_t launch_prefill_fp32(const WorkItem*, int64_t, const void*, const void*, const void*,
@@ -84,6 +84,10 @@ int main() {
                                                0, w, err);
                 checks += mla::build_work_list(qo.data(), kv.data(), batch, heads, causal, 64, 1,
                                                heads % 2 == 0 ? 2 : 1, w, err, true);
+                int per_wg = 0;
+                checks += mla::build_work_list(qo.data(), kv.data(), batch, heads, causal, 128, 8,
+                                               0, w, err, trial % 2 == 0, 512, &per_wg);
+                checks += w.size() % (8 * static_cast<size_t>(per_wg)) == 0;
                 const int s = mla::latent_kv_splits(qo.data(), kv.data(), batch, heads, causal,
                                                     128);
                 checks += mla::build_latent_work_list(qo.data(), kv.data(), batch, heads, causal,
@@ -106,6 +110,8 @@ int main() {
                 checks += mla_plan_info(p, &items, &bm, &nx, &hpi) == MLA_OK;
                 std::vector<int32_t> wbuf(static_cast<size_t>(items) * 8 + 8);
                 checks += mla_plan_items(p, wbuf.data(), items) == MLA_OK;
+                int32_t ipw = 0;
+                checks += mla_plan_items_per_workgroup(p, &ipw) == MLA_OK && (ipw == 1 || ipw == 2);
                 mla_plan_destroy(p);
                 mla_absorbed_plan* ap = nullptr;
                 checks += mla_absorbed_plan_create(&ap) == MLA_OK;

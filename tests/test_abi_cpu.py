@@ -128,6 +128,10 @@ def test_run_rejects_tensors_that_do_not_match_the_plan(q_rows, kv_rows, heads, 
 # work partitioner
 # ---------------------------------------------------------------------------
 
+# bf16 plans pair two light tiles while they see at most this many keys
+PAIR_MAX_KEYS = 512
+
+
 def _lim(r, diag0, kv_len):
     return min(kv_len, max(0, diag0 + r + 1))
 
@@ -161,13 +165,49 @@ def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8, heads_per_ite
         assert kv_hi == _lim(n_rows - 1, diag0, kv_len)
         cover[q_row0:q_row0 + n_rows, head0:head0 + n_heads] += 1
     assert np.all(cover == 1)
-    # XCD grouping: all tiles of one (sequence, head block) share index mod n_xcd
+    # XCD grouping: all tiles of one (sequence, head block) run on one XCD
+    # (workgroup w = entry // items_per_workgroup goes to XCD w mod n_xcd)
+    ipw = info["items_per_workgroup"]
+    # pairs a greedy walk up each sequence's sorted kv_hi values forms: two
+    # neighbours while they see at most PAIR_MAX_KEYS keys together
+    want_pairs = {}
+    for seq in range(len(qo) - 1):
+        hs = sorted(int(min(kv[seq + 1] - kv[seq],
+                            max(0, (kv[seq + 1] - kv[seq] - (qo[seq + 1] - qo[seq]) + r0 if causal
+                                    else kv[seq + 1] - kv[seq]) + min(bm, qo[seq + 1] - qo[seq] - r0))))
+                    for r0 in range(0, qo[seq + 1] - qo[seq], bm))
+        got, i = [], 0
+        while i < len(hs):
+            if i + 1 < len(hs) and hs[i] + hs[i + 1] <= PAIR_MAX_KEYS:
+                got.append((hs[i], hs[i + 1]))
+                i += 2
+            else:
+                i += 1
+        want_pairs[seq] = sorted(got)
+    pairing = dtype_name == "bf16" and nh == 1
+    any_pair = pairing and any(want_pairs.values())
+    assert ipw == (2 if any_pair else 1)
     idx = np.nonzero(items[:, 1] > 0)[0]
     groups = {}
     for i in idx:
-        groups.setdefault(_group(qo, items[i]), set()).add(i % n_xcd)
+        groups.setdefault(_group(qo, items[i]), set()).add((i // ipw) % n_xcd)
     assert all(len(v) == 1 for v in groups.values())
-    assert len(items) % n_xcd == 0
+    assert len(items) % (n_xcd * ipw) == 0
+    if ipw == 2:
+        # a workgroup's second entry, when present, follows a real first one
+        # of the same (sequence, head), the lighter tile first, and the pairs
+        # of every (sequence, head) are the greedy ones
+        got = {}
+        for w in range(len(items) // 2):
+            a, b = items[2 * w], items[2 * w + 1]
+            if b[1] == 0:
+                continue
+            assert a[1] > 0 and _group(qo, a) == _group(qo, b)
+            assert a[7] <= b[7] and a[7] + b[7] <= PAIR_MAX_KEYS
+            got.setdefault(_group(qo, a), []).append((int(a[7]), int(b[7])))
+        for seq in range(len(qo) - 1):
+            for h in range(heads):
+                assert sorted(got.get((seq, h), [])) == want_pairs[seq]
     return items, info
 
 
@@ -220,8 +260,10 @@ def test_partition_balances_xcds_and_orders_heaviest_first():
     qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     for hpi in (None, 4):
         items, info = _check_plan(qo, qo, 16, True, heads_per_item=hpi)
+        ipw = info["items_per_workgroup"]
+        xcd_of = (np.arange(len(items)) // ipw) % 8
         cost = np.where(items[:, 1] > 0, (items[:, 7] + 64) * items[:, 3], 0).astype(np.int64)
-        per_xcd = [cost[x::8].sum() for x in range(8)]
+        per_xcd = [cost[xcd_of == x].sum() for x in range(8)]
         group_cost = {}
         for it, c in zip(items, cost):
             if it[1] > 0:
@@ -231,7 +273,7 @@ def test_partition_balances_xcds_and_orders_heaviest_first():
         # inside one XCD queue the groups come heaviest first
         for x in range(8):
             seen = []
-            for it in items[x::8]:
+            for it in items[xcd_of == x]:
                 if it[1] > 0 and (not seen or seen[-1] != _group(qo, it)):
                     seen.append(_group(qo, it))
             costs = [group_cost[k] for k in seen]
@@ -242,7 +284,9 @@ def test_partition_without_xcd_grouping_has_no_padding():
     lens = [100, 700, 3]
     qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     items, info = _check_plan(qo, qo, 4, True, n_xcd=1)
-    assert np.all(items[:, 1] > 0) and info["n_xcd"] == 1
+    # every workgroup has work (only a single tile's partner entry is empty)
+    ipw = info["items_per_workgroup"]
+    assert np.all(items[::ipw, 1] > 0) and info["n_xcd"] == 1
 
 
 # ---------------------------------------------------------------------------
@@ -582,3 +626,40 @@ def test_decompress_prefill_rejects_invalid_arguments_before_any_hip_call():
     # query rows but no keys at all still need q and out, not the latent inputs
     nokeys = np.array([0, 0], dtype=np.int32)
     assert call(kvp=nokeys.ctypes.data, q=None) == 1
+
+
+def test_partition_pairs_light_tiles():
+    # causal: 300 tokens = tiles seeing 128, 256, 300 keys (one pair of the
+    # first two, one single); 4096 = 32 tiles (the 128 + 256 pair, 30
+    # singles); 100 = one tile (single)
+    lens = [300, 4096, 100]
+    qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    items, info = _check_plan(qo, qo, 2, True)
+    assert info["items_per_workgroup"] == 2
+    pairs = {0: 0, 1: 0, 2: 0}
+    singles = {0: 0, 1: 0, 2: 0}
+    for w in range(len(items) // 2):
+        a, b = items[2 * w], items[2 * w + 1]
+        if a[1] == 0:
+            continue
+        seq = _group(qo, a)[0]
+        if b[1] > 0:
+            pairs[seq] += 1
+        else:
+            singles[seq] += 1
+    assert pairs == {0: 2, 1: 2, 2: 0}           # per sequence over its 2 heads
+    assert singles == {0: 2, 1: 60, 2: 2}
+    # non-causal: 256 queries over 200 keys pair (400 keys); over 4096 keys
+    # nothing pairs and the list keeps one entry per workgroup
+    short = np.array([0, 256], dtype=np.int32)
+    _, info = _check_plan(short, np.array([0, 200], dtype=np.int32), 2, False)
+    assert info["items_per_workgroup"] == 2
+    _, info = _check_plan(short, np.array([0, 4096], dtype=np.int32), 2, False)
+    assert info["items_per_workgroup"] == 1
+    # rows that see no key (queries past the keys): their empty tiles pair
+    _check_plan(np.array([0, 300], dtype=np.int32), np.array([0, 2], dtype=np.int32), 2, True)
+    # fp32 plans and head blocks keep one entry per workgroup
+    _, info = _check_plan(qo, qo, 2, True, dtype_name="fp32")
+    assert info["items_per_workgroup"] == 1
+    _, info = _check_plan(qo, qo, 4, True, heads_per_item=2)
+    assert info["items_per_workgroup"] == 1

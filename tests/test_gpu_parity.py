@@ -96,6 +96,20 @@ def test_single_head(dtype, causal):
     _full_parity(x, f"one head dtype={dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_paired_workgroups_match_the_oracle(causal):
+    # bf16 plans run two light tiles of a sequence in one workgroup: here
+    # pairs of a full and a partial tile (22 rows, so three of the four
+    # waves have no row in it), pairs of tiles whose rows see no key
+    # (queries past the keys), lone tiles, and 1-row sequences
+    qo_lens = [150, 300, 1, 64, 280, 150]
+    kv_lens = [150, 300, 1, 64, 3, 100]
+    x = workloads.ragged_inputs(qo_lens, kv_lens, 3, torch.bfloat16, seed=71, causal=causal)
+    plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, 3, causal, torch.bfloat16)
+    assert plan.info()["items_per_workgroup"] == 2
+    _full_parity(x, f"paired workgroups causal={causal}")
+
+
 def _random_shape(rng):
     """A small random ragged batch: 1-6 sequences, lengths 0-600 (some empty),
     qo and kv drawn independently half of the time."""
