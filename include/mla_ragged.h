@@ -213,9 +213,11 @@ int mla_plan_info(const mla_plan *plan, int64_t *n_items, int32_t *block_m, int3
 int mla_plan_items(const mla_plan *plan, int32_t *dst, int64_t capacity_items);
 
 /* Work-list entries per workgroup (host only). A bf16 plan of one head per
- * item pairs two neighbouring light query tiles of a sequence (going up from
- * its lightest tile, while the keys the two see add up to at most 512) into
- * one workgroup: if any pair formed, entries 2w and 2w + 1 belong to
+ * item puts two query tiles of one sequence into one workgroup when
+ * (a) going up from the sequence's lightest tile, two neighbours see at most
+ * 512 keys together, or (b) all of its tiles see the same keys (non-causal),
+ * there are at least 8 of them and at most 4096 keys: then tiles 2k and
+ * 2k + 1 pair. If any pair formed, entries 2w and 2w + 1 belong to
  * workgroup w and run back to back (an entry 2w + 1 with n_rows == 0 is
  * absent) and this returns 2; otherwise, and for fp32 plans and head blocks,
  * entry w is workgroup w and it returns 1. The hardware hands workgroup w to

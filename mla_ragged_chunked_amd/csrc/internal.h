@@ -83,7 +83,8 @@ int prefill_fp32_block_m();
 // MI355X against one tile per workgroup: +7% on 64 sequences of 512 tokens
 // and 32 of 1024, +6% on 16 of 2048, +3% on 8 of 4096, +1% on the
 // DeepSeek-V3 batch; long, skewed and non-causal batches unchanged; caps
-// from 384 to 768 keys measured the same).
+// from 384 to 768 keys measured the same). The same switch also pairs the
+// equal tiles of non-causal sequences (planner.cpp, step 6).
 constexpr int kPrefillPairMaxKeys = 512;
 // `pair_max_keys` > 0 may pair tiles (see planner.cpp); `items_per_wg`, if
 // not NULL, receives the entries per workgroup slot of the list: 2 when a

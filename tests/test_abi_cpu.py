@@ -128,8 +128,12 @@ def test_run_rejects_tensors_that_do_not_match_the_plan(q_rows, kv_rows, heads, 
 # work partitioner
 # ---------------------------------------------------------------------------
 
-# bf16 plans pair two light tiles while they see at most this many keys
+# bf16 plans pair two light tiles while they see at most this many keys,
+# and the tiles of a sequence that all see the same keys when there are at
+# least PAIR_EQUAL_MIN_TILES of them over at most PAIR_EQUAL_MAX_KEYS keys
 PAIR_MAX_KEYS = 512
+PAIR_EQUAL_MIN_TILES = 8
+PAIR_EQUAL_MAX_KEYS = 4096
 
 
 def _lim(r, diag0, kv_len):
@@ -177,7 +181,11 @@ def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8, heads_per_ite
                                     else kv[seq + 1] - kv[seq]) + min(bm, qo[seq + 1] - qo[seq] - r0))))
                     for r0 in range(0, qo[seq + 1] - qo[seq], bm))
         got, i = [], 0
-        while i < len(hs):
+        if (len(hs) >= PAIR_EQUAL_MIN_TILES and hs[0] > 0 and hs[0] == hs[-1]
+                and kv[seq + 1] - kv[seq] <= PAIR_EQUAL_MAX_KEYS):
+            # every tile sees the same keys: neighbours pair
+            got = [(hs[0], hs[0])] * (len(hs) // 2)
+        while not got and i < len(hs):
             if i + 1 < len(hs) and hs[i] + hs[i + 1] <= PAIR_MAX_KEYS:
                 got.append((hs[i], hs[i + 1]))
                 i += 2
@@ -203,7 +211,7 @@ def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8, heads_per_ite
             if b[1] == 0:
                 continue
             assert a[1] > 0 and _group(qo, a) == _group(qo, b)
-            assert a[7] <= b[7] and a[7] + b[7] <= PAIR_MAX_KEYS
+            assert a[7] <= b[7] and (a[7] + b[7] <= PAIR_MAX_KEYS or a[7] == b[7])
             got.setdefault(_group(qo, a), []).append((int(a[7]), int(b[7])))
         for seq in range(len(qo) - 1):
             for h in range(heads):
@@ -628,7 +636,7 @@ def test_decompress_prefill_rejects_invalid_arguments_before_any_hip_call():
     assert call(kvp=nokeys.ctypes.data, q=None) == 1
 
 
-def test_partition_pairs_light_tiles():
+def test_partition_pairs_light_and_equal_tiles():
     # causal: 300 tokens = tiles seeing 128, 256, 300 keys (one pair of the
     # first two, one single); 4096 = 32 tiles (the 128 + 256 pair, 30
     # singles); 100 = one tile (single)
@@ -656,6 +664,18 @@ def test_partition_pairs_light_tiles():
     assert info["items_per_workgroup"] == 2
     _, info = _check_plan(short, np.array([0, 4096], dtype=np.int32), 2, False)
     assert info["items_per_workgroup"] == 1
+    # non-causal sequences whose tiles all see the same keys pair their
+    # neighbours from 8 tiles over at most 4096 keys on
+    for q_len, k_len, paired in [(1024, 4096, True), (1000, 4096, True), (896, 4096, False),
+                                 (1024, 4097, False), (2048, 100, True)]:
+        qo1 = np.array([0, q_len], dtype=np.int32)
+        kv1 = np.array([0, k_len], dtype=np.int32)
+        items1, info = _check_plan(qo1, kv1, 2, False)
+        assert info["items_per_workgroup"] == (2 if paired else 1)
+        if paired:
+            n_tiles = -(-q_len // 128)
+            n_pairs = sum(1 for w in range(len(items1) // 2) if items1[2 * w + 1][1] > 0)
+            assert n_pairs == 2 * (n_tiles // 2)     # over 2 heads
     # rows that see no key (queries past the keys): their empty tiles pair
     _check_plan(np.array([0, 300], dtype=np.int32), np.array([0, 2], dtype=np.int32), 2, True)
     # fp32 plans and head blocks keep one entry per workgroup

@@ -110,6 +110,17 @@ def test_paired_workgroups_match_the_oracle(causal):
     _full_parity(x, f"paired workgroups causal={causal}")
 
 
+def test_equal_tile_pairs_match_the_oracle():
+    # non-causal sequences of >= 8 tiles over <= 4096 keys pair neighbouring
+    # tiles (the last pair holds a 104-row tile); the short one pairs its
+    # two light tiles
+    qo_lens, kv_lens = [1000, 200], [1500, 300]
+    x = workloads.ragged_inputs(qo_lens, kv_lens, 2, torch.bfloat16, seed=72, causal=False)
+    plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, 2, False, torch.bfloat16)
+    assert plan.info()["items_per_workgroup"] == 2
+    _full_parity(x, "equal-tile pairs non-causal")
+
+
 def _random_shape(rng):
     """A small random ragged batch: 1-6 sequences, lengths 0-600 (some empty),
     qo and kv drawn independently half of the time."""
