@@ -49,3 +49,19 @@ def test_committed_profiles_match_the_kernel_sources(profile, source):
     # source hash matches the code; a kernel change needs a new profile
     traffic = bench.profile_traffic(profile, source)
     assert traffic is not None and traffic > 0
+
+
+def test_every_profile_names_the_current_source():
+    # each committed summary records the hash of the kernel source it was
+    # taken with; a kernel change needs a new profile
+    import glob
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    files = sorted(glob.glob(os.path.join(root, "profiles", "*.txt")))
+    assert files
+    for f in files:
+        fields = dict(line.split(": ", 1) for line in open(f).read().splitlines()[:6]
+                      if ": " in line)
+        assert "source" in fields and "source_code_sha256_16" in fields, f
+        src = os.path.join(root, fields["source"].strip())
+        assert bench.code_hash(src) == fields["source_code_sha256_16"].strip(), f
