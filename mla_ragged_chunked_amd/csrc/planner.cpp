@@ -38,9 +38,17 @@
 //       group then still runs several workgroups side by side over K/V
 //       that L2 holds (with few tiles over long keys, pairs halve that
 //       sharing and read the keys twice from HBM).
+//     Pairing is only used for batches of like sequences (every non-empty
+//     sequence within kPairMaxTilesPerSeq query tiles, the longest query and
+//     key lengths at most 1.5 times the shortest): the kernel form that runs
+//     two items is ~2-4% slower per tile than the one-item form (measured on
+//     MI355X with identical loop code; the compiler places the running-max
+//     chain differently), which pairing repays on such batches (+1 to +10%)
+//     but not on batches of mixed or long sequences (-1 to -4%).
 //     If any pair forms, the list holds two entries per workgroup slot
 //     (the second one empty for a lone tile), else one.
 #include <algorithm>
+#include <climits>
 #include <numeric>
 
 #include "internal.h"
@@ -54,6 +62,25 @@ constexpr int64_t kTileFixedCost = 64;   // Q load + epilogue, in key-equivalent
 // keys; with 4 tiles over 8192 keys pairing lost 10%, with 16 over 8192 2%)
 constexpr size_t kPairEqualMinTiles = 8;
 constexpr int32_t kPairEqualMaxKeys = 4096;
+constexpr int64_t kPairMaxTilesPerSeq = 32;
+
+// Whether the batch is one that pairing pays on (step 6): non-empty
+// sequences of at most kPairMaxTilesPerSeq query tiles whose longest query
+// and key lengths are within 1.5 times the shortest.
+bool pairing_pays(const int32_t* qo, const int32_t* kv, int batch, int block_m) {
+    int64_t q_min = INT64_MAX, q_max = 0, k_min = INT64_MAX, k_max = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t ql = qo[b + 1] - qo[b], kl = kv[b + 1] - kv[b];
+        if (ql == 0) continue;
+        q_min = std::min(q_min, ql);
+        q_max = std::max(q_max, ql);
+        k_min = std::min(k_min, kl);
+        k_max = std::max(k_max, kl);
+    }
+    if (q_max == 0) return false;
+    if ((q_max + block_m - 1) / block_m > kPairMaxTilesPerSeq) return false;
+    return 2 * q_max <= 3 * q_min && 2 * k_max <= 3 * k_min;
+}
 
 struct Tile {
     int32_t q_row0, n_rows, kv_start, kv_len, diag0, kv_hi, seq;
@@ -130,6 +157,8 @@ bool build_work_list(const int32_t* qo, const int32_t* kv, int batch, int num_he
     }
     std::stable_sort(groups.begin(), groups.end(),
                      [](const Group& a, const Group& c) { return a.cost > c.cost; });
+
+    if (pair_max_keys > 0 && !pairing_pays(qo, kv, batch, block_m)) pair_max_keys = 0;
 
     // Workgroup units of every sequence: one tile, or a pair of light tiles
     // (the lighter one first); heaviest unit first. -1 marks no second tile.

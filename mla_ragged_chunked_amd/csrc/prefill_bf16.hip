@@ -387,12 +387,14 @@ void prefill_bf16_kernel(const WorkItem* __restrict__ items,
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
         }
         if constexpr (kMasked) {
-            const int key0 = kt * kBN;
+            // slot i holds key kt * kBN + (i/4) * 8 + 4 g + i%4: it is visible
+            // iff its offset (i/4) * 8 + i%4 inside the tile is below lim_rel,
+            // so each compare takes an inline constant and no per-slot key
+            // has to stay in a register
+            const int lim_rel = my_lim - kt * kBN - g * 4;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + (i >> 2) * 8 + g * 4 + (i & 3);
-                sacc[i] = key < my_lim ? sacc[i] : -INFINITY;
-            }
+            for (int i = 0; i < 16; ++i)
+                sacc[i] = (i >> 2) * 8 + (i & 3) < lim_rel ? sacc[i] : -INFINITY;
         }
     };
     auto tile_max = [&](const f32x16_t& sv) {

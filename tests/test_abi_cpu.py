@@ -136,6 +136,19 @@ PAIR_EQUAL_MIN_TILES = 8
 PAIR_EQUAL_MAX_KEYS = 4096
 
 
+def _pairing_pays(qo, kv, bm):
+    """Pairing is used only for batches of like sequences: every non-empty
+    sequence within 32 query tiles, longest query and key lengths at most
+    1.5 times the shortest."""
+    ql = [int(qo[b + 1] - qo[b]) for b in range(len(qo) - 1)]
+    kl = [int(kv[b + 1] - kv[b]) for b in range(len(qo) - 1)]
+    live = [b for b in range(len(ql)) if ql[b] > 0]
+    if not live:
+        return False
+    qs, ks = [ql[b] for b in live], [kl[b] for b in live]
+    return -(-max(qs) // bm) <= 32 and 2 * max(qs) <= 3 * min(qs) and 2 * max(ks) <= 3 * min(ks)
+
+
 def _lim(r, diag0, kv_len):
     return min(kv_len, max(0, diag0 + r + 1))
 
@@ -192,7 +205,9 @@ def _check_plan(qo, kv, heads, causal, dtype_name="bf16", n_xcd=8, heads_per_ite
             else:
                 i += 1
         want_pairs[seq] = sorted(got)
-    pairing = dtype_name == "bf16" and nh == 1
+    pairing = dtype_name == "bf16" and nh == 1 and _pairing_pays(qo, kv, bm)
+    if not pairing:
+        want_pairs = {seq: [] for seq in want_pairs}
     any_pair = pairing and any(want_pairs.values())
     assert ipw == (2 if any_pair else 1)
     idx = np.nonzero(items[:, 1] > 0)[0]
@@ -637,10 +652,10 @@ def test_decompress_prefill_rejects_invalid_arguments_before_any_hip_call():
 
 
 def test_partition_pairs_light_and_equal_tiles():
-    # causal: 300 tokens = tiles seeing 128, 256, 300 keys (one pair of the
-    # first two, one single); 4096 = 32 tiles (the 128 + 256 pair, 30
-    # singles); 100 = one tile (single)
-    lens = [300, 4096, 100]
+    # causal, like sequences: 300 tokens = tiles seeing 128, 256, 300 keys
+    # (one pair of the first two, one single); 260 = tiles of 128, 256, 260
+    # keys (the same); 384 = 128, 256, 384 (the same)
+    lens = [300, 260, 384]
     qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     items, info = _check_plan(qo, qo, 2, True)
     assert info["items_per_workgroup"] == 2
@@ -655,8 +670,13 @@ def test_partition_pairs_light_and_equal_tiles():
             pairs[seq] += 1
         else:
             singles[seq] += 1
-    assert pairs == {0: 2, 1: 2, 2: 0}           # per sequence over its 2 heads
-    assert singles == {0: 2, 1: 60, 2: 2}
+    assert pairs == {0: 2, 1: 2, 2: 2}           # per sequence over its 2 heads
+    assert singles == {0: 2, 1: 2, 2: 2}
+    # mixed or long batches keep one tile per workgroup
+    for mixed in ([300, 4096, 100], [5000, 5000], [300, 500]):
+        q = np.concatenate([[0], np.cumsum(mixed)]).astype(np.int32)
+        _, info = _check_plan(q, q, 2, True)
+        assert info["items_per_workgroup"] == 1
     # non-causal: 256 queries over 200 keys pair (400 keys); over 4096 keys
     # nothing pairs and the list keeps one entry per workgroup
     short = np.array([0, 256], dtype=np.int32)
@@ -677,7 +697,8 @@ def test_partition_pairs_light_and_equal_tiles():
             n_pairs = sum(1 for w in range(len(items1) // 2) if items1[2 * w + 1][1] > 0)
             assert n_pairs == 2 * (n_tiles // 2)     # over 2 heads
     # rows that see no key (queries past the keys): their empty tiles pair
-    _check_plan(np.array([0, 300], dtype=np.int32), np.array([0, 2], dtype=np.int32), 2, True)
+    _, info = _check_plan(np.array([0, 300], dtype=np.int32), np.array([0, 2], dtype=np.int32), 2, True)
+    assert info["items_per_workgroup"] == 2
     # fp32 plans and head blocks keep one entry per workgroup
     _, info = _check_plan(qo, qo, 2, True, dtype_name="fp32")
     assert info["items_per_workgroup"] == 1

@@ -96,29 +96,30 @@ def test_single_head(dtype, causal):
     _full_parity(x, f"one head dtype={dtype} causal={causal}")
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_paired_workgroups_match_the_oracle(causal):
-    # bf16 plans run two light tiles of a sequence in one workgroup: here
-    # pairs of a full and a partial tile (22 rows, so three of the four
-    # waves have no row in it), pairs of tiles whose rows see no key
-    # (queries past the keys), lone tiles, and 1-row sequences
-    qo_lens = [150, 300, 1, 64, 280, 150]
-    kv_lens = [150, 300, 1, 64, 3, 100]
-    x = workloads.ragged_inputs(qo_lens, kv_lens, 3, torch.bfloat16, seed=71, causal=causal)
+# bf16 plans pair two tiles of a sequence in one workgroup on batches of
+# like sequences; each case below is such a batch
+PAIRED_CASES = [
+    # a full and a partial tile (22 rows: three of the four waves have no
+    # row in it), causal and non-causal (non-causal: the partial tile first)
+    ([150, 150, 140], [150, 150, 140], True),
+    ([150, 150], [100, 120], False),
+    # queries past the keys: pairs of tiles whose rows see no key
+    ([280, 300], [3, 4], True),
+    # a full tile paired with a tile of one or two rows
+    ([129, 129, 130], [129, 129, 130], True),
+    # non-causal sequences of >= 8 tiles over <= 4096 keys: all neighbours
+    # pair (the last pair holds a 104-row tile)
+    ([1000, 1000], [1500, 1400], False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PAIRED_CASES)))
+def test_paired_workgroups_match_the_oracle(case):
+    qo_lens, kv_lens, causal = PAIRED_CASES[case]
+    x = workloads.ragged_inputs(qo_lens, kv_lens, 3, torch.bfloat16, seed=71 + case, causal=causal)
     plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, 3, causal, torch.bfloat16)
     assert plan.info()["items_per_workgroup"] == 2
-    _full_parity(x, f"paired workgroups causal={causal}")
-
-
-def test_equal_tile_pairs_match_the_oracle():
-    # non-causal sequences of >= 8 tiles over <= 4096 keys pair neighbouring
-    # tiles (the last pair holds a 104-row tile); the short one pairs its
-    # two light tiles
-    qo_lens, kv_lens = [1000, 200], [1500, 300]
-    x = workloads.ragged_inputs(qo_lens, kv_lens, 2, torch.bfloat16, seed=72, causal=False)
-    plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, 2, False, torch.bfloat16)
-    assert plan.info()["items_per_workgroup"] == 2
-    _full_parity(x, "equal-tile pairs non-causal")
+    _full_parity(x, f"paired workgroups case {case}")
 
 
 def _random_shape(rng):
