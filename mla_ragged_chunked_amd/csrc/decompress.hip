@@ -260,16 +260,6 @@ void decompress_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __rest
                     *reinterpret_cast<const bf16x8_t*>(st + b_base + cslot(l32, 2 * (ks + kPrefetch) + g) * 16);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], b, acc, 0, 0, 0);
         }
-        // Keep the fragment reads kPrefetch MFMAs ahead: left alone, the
-        // scheduler moves each read next to its MFMA, which then waits for
-        // the LDS (measured on MI355X: 1.22 -> 1.18 ms, bit-identical).
-        __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);   // DS reads
-#pragma unroll
-        for (int q = 0; q < kKSteps - kPrefetch; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // one DS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
         // v_permlane32_swap exchanges the upper 32 lanes of its first operand
         // with the lower 32 lanes of its second: lane g = 0 ends with dims
         // 16 pr + 0..7, lane g = 1 with 16 pr + 8..15
