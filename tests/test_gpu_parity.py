@@ -189,6 +189,37 @@ def test_more_heads_and_large_scores():
     _full_parity(x, "sm_scale 1e-3")
 
 
+def _rising_keys(k, kv_indptr, dim, step):
+    """Key j of a sequence of L keys holds step * (j - (L - 1)) in `dim`
+    (every head): rising scores that end near 0, so a row that sees the
+    whole sequence has an LSE of a few units."""
+    for b in range(len(kv_indptr) - 1):
+        ks, ke = kv_indptr[b], kv_indptr[b + 1]
+        j = torch.arange(ke - ks, dtype=torch.float64) - (ke - ks - 1)
+        k[ks:ke, ..., dim] = (step * j).to(k.dtype).view(-1, *([1] * (k.dim() - 2)))
+
+
+# fp32 only without the causal mask: early causal rows stop far below the
+# last key, with LSEs of -75, where one fp32 ulp is near the 1e-5 tolerance
+@pytest.mark.parametrize("dtype,causal", [(torch.bfloat16, True), (torch.bfloat16, False),
+                                          (torch.float32, False)])
+def test_running_max_rises_on_every_tile(dtype, causal):
+    # Scores climb by ~8 (natural log units) per 32-key tile: every query
+    # holds 1 in dim 0 and key j holds (j - last) / 4 there, the other query
+    # dims are small noise. The running max then moves past the lazy
+    # threshold on nearly every tile, so the O rescale runs on nearly every
+    # tile.
+    lens_q, lens_kv = [300, 129, 64, 1], [300, 129, 64, 700]
+    x = workloads.ragged_inputs(lens_q, lens_kv, 3, dtype, seed=41, causal=causal, sm_scale=1.0)
+    q, k = x.q.clone(), x.k.clone()
+    q.mul_(0.05)
+    q[..., 0] = 1.0
+    _rising_keys(k, x.kv_indptr, 0, 0.25)
+    x = workloads.PrefillInputs(q, k, x.v, x.qo_indptr, x.kv_indptr, x.num_heads, x.causal,
+                                x.sm_scale)
+    _full_parity(x, f"rising scores {dtype} causal={causal}")
+
+
 def test_plan_run_matches_one_shot_and_repeats():
     lens = [300, 1, 129]
     x = _to(workloads.ragged_inputs(lens, lens, 4, torch.bfloat16, seed=37), DEV)
@@ -902,6 +933,25 @@ def test_absorbed_scale_extremes():
     for scale in (1.0, 1e-3):
         x = workloads.absorbed_inputs(lens, lens, 4, seed=14, causal=True, sm_scale=scale)
         _absorbed_parity(x, f"sm_scale {scale}")
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_absorbed_running_max_rises_on_every_tile(decode):
+    # As for the MHA pass: scores climb by ~8 per 32-key tile, carried by a
+    # RoPE dim (512) that the values do not include, so the in-place AGPR
+    # rescale of O runs on nearly every tile; the decode shape also splits
+    # the keys (each split rescales on its own, then the splits merge).
+    if decode:
+        lens_q, lens_kv = [1, 1, 1, 1], [2048, 1000, 3000, 64]
+    else:
+        lens_q, lens_kv = [300, 129, 64], [300, 129, 700]
+    x = workloads.absorbed_inputs(lens_q, lens_kv, 4, seed=43, causal=True, sm_scale=1.0)
+    q, kv = x.q.clone(), x.kv.clone()
+    q.mul_(0.05)
+    q[..., 512] = 1.0
+    _rising_keys(kv, x.kv_indptr, 512, 0.25)
+    x = workloads.AbsorbedInputs(q, kv, x.qo_indptr, x.kv_indptr, x.num_heads, x.causal, x.sm_scale)
+    _absorbed_parity(x, f"rising scores decode={decode}")
 
 
 def test_absorbed_batch_full_size_sampled():
