@@ -158,10 +158,11 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
 
     // Q fragments (B operand): this lane's row, dims 16 s + 8 g .. +8; rows
     // past the tile's end load its last row (their results are never stored).
-    // Plain loads, issued after the first two K/V tiles and completed by a
-    // compiler-visible wait before the key loop: the compiler then sees no
-    // Q load in flight and puts no waits of its own inside the loop (those
-    // would also drain the tiles in flight).
+    // Plain loads, issued after the first K/V tiles and completed by a wait
+    // before the key loop; the registers then pass through an empty asm
+    // (below), without which the compiler kept counting the loads as in
+    // flight and waited for them before the score MFMAs of every tile
+    // (waits that also drained the ring's tiles in flight).
     bf16x8_t qf[kKSteps];
     const bf16x8_t* q_src;
     {
@@ -376,6 +377,12 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     // s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their maxima): Q and
     // the first tiles have all landed
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
+    // The empty asm redefines the Q registers after that wait, so the
+    // compiler no longer sees loads in flight into them and puts none of its
+    // own vmcnt waits in the loop (those would also wait for the ring's
+    // tiles in flight, issued as asm it does not count).
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+v"(qf[s]));
 
     int j = 0;
     // with_o: O may already hold earlier tiles (false for the first one)
@@ -412,9 +419,16 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
     if (wave_rows <= 0) return;
     const float ltot = xor32_sum(l_run);
-    if (my_row >= it.n_rows) return;
+    // The lane's row and half are recomputed here, by an asm the compiler
+    // cannot merge with the one at the top, so no lane-dependent index stays
+    // live (or spilled) across the key loop.
+    int lane_e;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+    const int g_e = lane_e >> 5;
+    const int row_e = row_w0 + (lane_e & 31);
+    if (row_e >= it.n_rows) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
-    const int64_t rho = (int64_t)it.row0 + my_row;
+    const int64_t rho = (int64_t)it.row0 + row_e;
     if (it.part >= 0) {
         // a KV split: fp32 partial state over this item's keys
         float* pdst = part_o + ((int64_t)it.part * part_rows + rho) * kDv;
@@ -422,14 +436,14 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
         for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-                const int dv = db * 32 + grp * 8 + g * 4;
+                const int dv = db * 32 + grp * 8 + g_e * 4;
                 f32x4_t o4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o4[e] = oacc[db][grp * 4 + e] * inv;
                 *reinterpret_cast<f32x4_t*>(pdst + dv) = o4;
             }
         }
-        if (g == 0)
+        if (g_e == 0)
             part_lse[(int64_t)it.part * part_rows + rho] =
                 ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
         return;
@@ -439,14 +453,14 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
-            const int dv = db * 32 + grp * 8 + g * 4;
+            const int dv = db * 32 + grp * 8 + g_e * 4;
             bf16x4_t o4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][grp * 4 + e] * inv);
             *reinterpret_cast<bf16x4_t*>(dst + dv) = o4;
         }
     }
-    if (g == 0 && lse != nullptr) lse[rho] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
+    if (g_e == 0 && lse != nullptr) lse[rho] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
