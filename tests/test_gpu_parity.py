@@ -220,6 +220,35 @@ def test_running_max_rises_on_every_tile(dtype, causal):
     _full_parity(x, f"rising scores {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("paired", [False, True])
+def test_running_max_rises_paired_and_paged(paired):
+    # The same forced rescale through the two-item kernel form (a batch of
+    # like sequences, whose light tiles pair) or the one-item form, against
+    # the oracle, and through the page pool, bit for bit against the
+    # contiguous call (the paged kernels are separate instantiations).
+    if paired:
+        lens_q = lens_kv = [300, 260, 384]
+    else:
+        lens_q, lens_kv = [300, 129, 64, 1], [300, 129, 64, 700]
+    x = workloads.ragged_inputs(lens_q, lens_kv, 3, torch.bfloat16, seed=47, causal=True,
+                                sm_scale=1.0)
+    q, k = x.q.clone(), x.k.clone()
+    q.mul_(0.05)
+    q[..., 0] = 1.0
+    _rising_keys(k, x.kv_indptr, 0, 0.25)
+    x = workloads.PrefillInputs(q, k, x.v, x.qo_indptr, x.kv_indptr, x.num_heads, x.causal,
+                                x.sm_scale)
+    plan = mra.Plan().plan(x.qo_indptr, x.kv_indptr, 3, True, torch.bfloat16)
+    assert plan.info()["items_per_workgroup"] == (2 if paired else 1)
+    _full_parity(x, f"rising scores paired={paired}")
+    g = _to(x, DEV)
+    kc, vc, table = _paged_cache(g, 64, extra_pages=2, seed=5)
+    ref_o, ref_l = mra.ragged_prefill(g.q, g.k, g.v, x.qo_indptr, x.kv_indptr, True, 1.0)
+    o, l = mra.ragged_prefill_paged(g.q, kc, vc, x.qo_indptr, x.kv_indptr, table, True, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
 def test_plan_run_matches_one_shot_and_repeats():
     lens = [300, 1, 129]
     x = _to(workloads.ragged_inputs(lens, lens, 4, torch.bfloat16, seed=37), DEV)
