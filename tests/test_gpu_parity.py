@@ -728,6 +728,29 @@ def test_decompress_prefill_small_parity(lens_q, lens_kv, heads, causal):
     check(o, lse, o2.double().cpu(), lse2.double().cpu(), torch.bfloat16, "fused vs two-call")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_decompress_prefill_running_max_rises_on_every_tile(causal):
+    # The forced rescale of the MHA tests through the fused kernel: the keys'
+    # RoPE dims come straight from k_rope, so k_rope dim 0 rises with the key
+    # index against queries holding 1 in dim 128 (scores climb ~8 per tile).
+    lens_q, lens_kv = [300, 129, 64], [300, 129, 700]
+    x = workloads.latent_prefill_inputs(lens_q, lens_kv, 2, seed=19, causal=causal)
+    q, k_rope = x.q.clone(), x.k_rope.clone()
+    q.mul_(0.05)
+    q[..., 128] = 1.0
+    _rising_keys(k_rope, x.kv_indptr, 0, 0.25)
+    x = workloads.LatentPrefillInputs(x.c_kv, k_rope, x.w_uk, x.w_uv, q, x.qo_indptr,
+                                      x.kv_indptr, x.num_heads, causal, 1.0)
+    g = _latent_to(x, DEV)
+    _flush(f"[gpu] fused decompress+prefill, rising scores, causal={causal}")
+    o, lse = mra.decompress_prefill(g.q, g.c_kv, g.k_rope, g.w_uk, g.w_uv, x.qo_indptr,
+                                    x.kv_indptr, causal, x.sm_scale)
+    torch.cuda.synchronize()
+    rk, rv = oracle.decompress(x.c_kv, x.k_rope, x.w_uk, x.w_uv, x.num_heads)     # fp64
+    ro, rl = oracle.prefill(x.q.double(), rk, rv, x.qo_indptr, x.kv_indptr, causal, x.sm_scale)
+    check(o, lse, ro, rl, torch.bfloat16, "fused decompress+prefill, rising scores")
+
+
 def test_decompress_prefill_without_lse():
     x = workloads.latent_prefill_inputs([70, 9], [100, 9], 2, seed=12, causal=True)
     g = _latent_to(x, DEV)
