@@ -109,28 +109,18 @@ __device__ __forceinline__ int lim_of(int r, int diag0, int kv_len) {
 __device__ __forceinline__ int vslot(int row, int c) { return c ^ ((row & 3) << 2); }
 
 // One 16-byte-per-lane global -> LDS load: lane l's 16 bytes land at
-// lds_base + 16 * l. Issued as inline asm so the compiler does not see LDS
-// DMA in flight (it would wait for all of it before every LDS read); the
-// kernel waits for completion itself with wait_vmcnt before the barrier
-// that publishes a tile. Nothing else in this kernel uses M0.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds_dst) {
-    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    const uint64_t b = (uint64_t)(uintptr_t)sbase;
-    // readfirstlane returns int: take each half as uint32_t before widening,
-    // or a low word with bit 31 set would sign-extend into the high word
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds_addr), "v"(voff), "s"(base) : "memory", "m0");
-}
-
-// The same load with M0 = lds_base + OFF set by one scalar add (lds_base
-// and sbase are wave-uniform values already in SGPRs).
+// lds_base + OFF + 16 * l, M0 set by one scalar add (lds_base and sbase are
+// wave-uniform values already in SGPRs). Issued as inline asm so the
+// compiler does not see LDS DMA in flight (it would wait for all of it
+// before every LDS read); the kernel waits for completion itself with
+// wait_vmcnt before the barrier that publishes a tile. Nothing else in this
+// kernel uses M0.
 template <int OFF>
 __device__ __forceinline__ void dma16o(const void* sbase, uint32_t voff, uint32_t lds_base) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
     const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    // readfirstlane returns int: take each half as uint32_t before widening,
+    // or a low word with bit 31 set would sign-extend into the high word
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
     const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
