@@ -16,7 +16,7 @@
 //    the transposed weights of 32 output dims for all 512 latent dims in
 //    registers for the whole kernel (32 MFMA A operands, 128 VGPRs), loaded
 //    once through LDS with transposing reads.
-//  * The latent cache streams through a 3-stage LDS ring in tiles of 32
+//  * The latent cache streams through a 4-stage LDS ring in tiles of 32
 //    tokens (32 KB of c_kv + 4 KB of k_rope per tile) loaded straight from
 //    HBM with global_load_lds_dwordx4; every wave reads the whole tile as
 //    the B operand (c_kv rows XOR-swizzled by token: conflict-free 16-byte
@@ -62,7 +62,7 @@ constexpr int kCRowB = kDlat * 2;               // 1 KB: one token's latent
 constexpr int kCBytes = kTT * kCRowB;           // 32 KB
 constexpr int kRBytes = kTT * kDrope * 2;       // 4 KB of k_rope per tile
 constexpr int kStage = kCBytes + kRBytes;       // 36 KB
-constexpr int kStages = 3;                      // 108 KB ring
+constexpr int kStages = 4;                      // 144 KB ring
 constexpr int kLds = kStages * kStage;
 constexpr int kWRowB = kNB * 2;                 // 512 B: one latent row of the W block
 constexpr int kWRound = 128;                    // latent rows of W per load round (64 KB)
@@ -210,27 +210,32 @@ void decompress_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __rest
     const int out_dim = is_v ? kDvo : kDqk;
     uint16_t* dst_base = is_v ? v_out : k_out;
 
-    // Vector-memory ops of a wave, in issue order: the DMA of tiles 0 and 1,
-    // then per iteration i the DMA of tile i+2 (4 ops, 5 for waves 0-3) at
-    // its top and the stores of tile i at its end (2 output stores; K blocks
-    // 1 more of k_rope). Every op but the last tile's has an active lane, so
-    // the counts are exact: after tile i's DMA come DMA(1) (i = 0), S(0) and
-    // DMA(2) (i = 1), or S(i-2), DMA(i+1) and S(i-1) (i >= 2). The wait for
-    // tile i leaves those in flight.
+    // Vector-memory ops of a wave, in issue order: the DMA of tiles 0, 1 and
+    // 2, then per iteration i the DMA of tile i+3 (D = 4 ops, 5 for waves
+    // 0-3) at its top and the stores S(i) of tile i at its end (2 output
+    // stores; K blocks 1 more of k_rope). Every op but the last tile's has an
+    // active lane, so the counts are exact: after tile i's DMA come DMA(1),
+    // DMA(2) (i = 0); DMA(2), DMA(3), S(0) (i = 1); DMA(3), S(0), DMA(4),
+    // S(1) (i = 2); S(i-3), DMA(i+1), S(i-2), DMA(i+2), S(i-1) (i >= 3). The
+    // wait for tile i leaves those in flight; near the end (i + 2 >= tiles)
+    // it waits for everything.
     auto wait_tile = [&](int i) {
-        if (i + 1 >= n_tiles) { wait_vmcnt<0>(); return; }
+        if (i + 2 >= n_tiles) { wait_vmcnt<0>(); return; }
         const int st_ = !wave_active ? 0 : (is_v ? 2 : 3);
         const int d_ = rope_loader ? kCLoads + 1 : kCLoads;
-        const int after = i == 0 ? d_ : (i == 1 ? d_ + st_ : d_ + 2 * st_);
+        const int after = 2 * d_ + (i < 3 ? i : 3) * st_;
         switch (after) {
-            case 4: wait_vmcnt<4>(); break;
-            case 5: wait_vmcnt<5>(); break;
-            case 6: wait_vmcnt<6>(); break;
-            case 7: wait_vmcnt<7>(); break;
             case 8: wait_vmcnt<8>(); break;
-            case 9: wait_vmcnt<9>(); break;
             case 10: wait_vmcnt<10>(); break;
             case 11: wait_vmcnt<11>(); break;
+            case 12: wait_vmcnt<12>(); break;
+            case 13: wait_vmcnt<13>(); break;
+            case 14: wait_vmcnt<14>(); break;
+            case 15: wait_vmcnt<15>(); break;
+            case 16: wait_vmcnt<16>(); break;
+            case 17: wait_vmcnt<17>(); break;
+            case 18: wait_vmcnt<18>(); break;
+            case 19: wait_vmcnt<19>(); break;
             default: wait_vmcnt<0>(); break;
         }
     };
@@ -241,10 +246,11 @@ void decompress_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __rest
 
     if (n_tiles > 0) issue(0);
     if (n_tiles > 1) issue(1);
+    if (n_tiles > 2) issue(2);
     for (int i = 0; i < n_tiles; ++i) {
         wait_tile(i);
         __syncthreads();
-        if (i + 2 < n_tiles) issue(i + 2);   // into tile i-1's stage, retired by the barrier
+        if (i + 3 < n_tiles) issue(i + 3);   // into tile i-1's stage, retired by the barrier
         if (!wave_active) continue;
         const uint8_t* st = smem + (i % kStages) * kStage;
         bf16x8_t bq[kPrefetch];
