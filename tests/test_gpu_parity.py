@@ -7,6 +7,7 @@ properties that hold at any size. Inputs come from the seeded generators in
 """
 import math
 import os
+import random
 
 import pytest
 import torch
@@ -547,6 +548,28 @@ def test_merge_state_parity(dtype):
     torch.cuda.synchronize()
     ro, rl = oracle.merge(o_a, l_a, o_b, l_b)
     check(o, l, ro, rl, dtype, f"merge {dtype}")
+
+
+def test_merge_state_beyond_one_pass():
+    # More rows than one pass of the merge grid covers (2^20 workgroups of
+    # 256 lanes at 16 lanes per bf16 row: 2^24 rows, i.e. 131072 tokens of
+    # 128 heads), so the grid-stride loop runs; rows of both passes, some
+    # with an empty side, are checked against the oracle.
+    heads = 128
+    tokens = (1 << 24) // heads + 64
+    _flush(f"[gpu] merge_state beyond one pass: {tokens} tokens x {heads} heads")
+    o_a, l_a, o_b, l_b = workloads.merge_inputs(tokens, heads, torch.bfloat16, seed=44, device=DEV,
+                                                neg_inf_frac=0.05)
+    o, l = mra.merge_state(o_a, l_a, o_b, l_b)
+    torch.cuda.synchronize()
+    rng = random.Random(9)
+    pick = {0, 1, tokens // 2, (1 << 24) // heads - 1} | set(range(tokens - 64, tokens))
+    pick |= {rng.randrange(tokens) for _ in range(64)}
+    idx = torch.tensor(sorted(pick), device=DEV)
+    ro, rl = oracle.merge(o_a[idx].cpu(), l_a[idx].cpu(), o_b[idx].cpu(), l_b[idx].cpu())
+    check(o[idx], l[idx], ro, rl, torch.bfloat16, "merge beyond one pass")
+    del o_a, l_a, o_b, l_b, o, l
+    torch.cuda.empty_cache()
 
 
 def test_merge_state_in_place():
