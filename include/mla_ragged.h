@@ -395,8 +395,10 @@ int mla_decompress_prefill(const void *q, const void *c_kv, const void *k_rope, 
  *   the row tiles alone
  *   cannot fill the GPU (e.g. a decode step, one token per sequence), the
  *   keys of each tile are split over up to 32 work items (flash-decoding
- *   style); their fp32 partial states go to a library-owned, grow-only
- *   buffer per (device, stream) and a second kernel merges them.
+ *   style); their partial states (O in bf16, normalised; LSE in fp32) go to
+ *   a library-owned, grow-only buffer per (device, stream) and a second
+ *   kernel merges them (one more bf16 rounding of each partial O before the
+ *   weighted sum).
  */
 int mla_absorbed_prefill(const void *q, const void *kv, const int32_t *qo_indptr,
                          const int32_t *kv_indptr, int32_t batch, int32_t num_heads,

@@ -485,8 +485,9 @@ int absorbed_upload(mla_absorbed_plan* p, hipStream_t stream) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (p->splits > 1) {
+        // per split and row: O in bf16, LSE in fp32
         const size_t need = static_cast<size_t>(p->splits) * static_cast<size_t>(p->rows) *
-                            (MLA_LATENT_DIM + 1) * sizeof(float);
+                            (MLA_LATENT_DIM * sizeof(uint16_t) + sizeof(float));
         if (p->part_device != -1 && p->part_device != dev) {
             // the plan moves to another device: its last run must end first
             p->last_run.wait();
@@ -548,11 +549,14 @@ int absorbed_run(const mla_absorbed_plan* p, const void* q, const void* kv, int6
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (dev != p->dwl.device || (p->splits > 1 && dev != p->part_device))
         return fail(MLA_ESTATE, "plan was uploaded on another device");
-    float* part_o = nullptr;
+    uint16_t* part_o = nullptr;
     float* part_lse = nullptr;
     if (p->splits > 1) {
-        part_o = static_cast<float*>(p->part);
-        part_lse = part_o + static_cast<size_t>(p->splits) * p->rows * MLA_LATENT_DIM;
+        // the O block is splits x rows x 512 bf16 (a multiple of 1 KB), so
+        // the LSE block after it stays 16-byte aligned
+        part_o = static_cast<uint16_t*>(p->part);
+        part_lse = reinterpret_cast<float*>(part_o + static_cast<size_t>(p->splits) * p->rows *
+                                                         MLA_LATENT_DIM);
     }
     e = mla::launch_prefill_absorbed(p->dwl.dev, static_cast<int64_t>(p->items.size()), q, kv,
                                      out, lse, p->num_heads, sm_scale, stream, pg, part_o,

@@ -143,16 +143,17 @@ hipError_t launch_prefill_fp32(const WorkItem* items, int64_t n_items, const voi
                                const PagedKv* paged = nullptr);
 // `paged` == nullptr: contiguous cache [Tk, 576] (rows from kv_start); else
 // a page pool [num_pages, page_size, 576] (PagedKv with H = 1).
-// Items with part >= 0 write fp32 partials: O to part_o[(part * part_rows
-// + rho) * 512], LSE to part_lse[part * part_rows + rho].
+// Items with part >= 0 write partial states: O (bf16, normalised) to
+// part_o[(part * part_rows + rho) * 512], LSE (fp32) to
+// part_lse[part * part_rows + rho].
 hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, const void* q,
                                    const void* kv, void* out, float* lse, int num_heads,
                                    float sm_scale, hipStream_t stream,
-                                   const PagedKv* paged = nullptr, float* part_o = nullptr,
+                                   const PagedKv* paged = nullptr, uint16_t* part_o = nullptr,
                                    float* part_lse = nullptr, int64_t part_rows = 0);
 // Combine `splits` partial states per row into out (bf16 [rows, 512]) and lse
 // (fp32 [rows], may be NULL).
-hipError_t launch_merge_splits(const float* part_o, const float* part_lse, int splits,
+hipError_t launch_merge_splits(const uint16_t* part_o, const float* part_lse, int splits,
                                int64_t rows, void* out, float* lse, hipStream_t stream);
 hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b,
                         const float* lse_b, void* o, float* lse, int64_t num_rows,

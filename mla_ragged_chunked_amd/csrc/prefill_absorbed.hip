@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_t* __restrict__ q,
                              const uint16_t* __restrict__ kv, uint16_t* __restrict__ out,
                              float* __restrict__ lse, int num_heads, float scale_log2, PagedKv pg,
-                             const int32_t* __restrict__ block_table, float* __restrict__ part_o,
+                             const int32_t* __restrict__ block_table, uint16_t* __restrict__ part_o,
                              float* __restrict__ part_lse, int64_t part_rows) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
 
@@ -431,26 +431,10 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
     if (row_e >= it.n_rows) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.0f;
     const int64_t rho = (int64_t)it.row0 + row_e;
-    if (it.part >= 0) {
-        // a KV split: fp32 partial state over this item's keys
-        float* pdst = part_o + ((int64_t)it.part * part_rows + rho) * kDv;
-#pragma unroll
-        for (int db = 0; db < kDvBlocks; ++db) {
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const int dv = db * 32 + grp * 8 + g_e * 4;
-                f32x4_t o4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = oacc[db][grp * 4 + e] * inv;
-                *reinterpret_cast<f32x4_t*>(pdst + dv) = o4;
-            }
-        }
-        if (g_e == 0)
-            part_lse[(int64_t)it.part * part_rows + rho] =
-                ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
-        return;
-    }
-    uint16_t* dst = out + rho * kDv;
+    // a KV split writes its partial state over this item's keys: O (bf16,
+    // normalised like a final output) and its LSE (fp32)
+    const bool split = it.part >= 0;
+    uint16_t* dst = split ? part_o + ((int64_t)it.part * part_rows + rho) * kDv : out + rho * kDv;
 #pragma unroll
     for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
@@ -462,7 +446,9 @@ void prefill_absorbed_kernel(const LatentItem* __restrict__ items, const uint16_
             *reinterpret_cast<bf16x4_t*>(dst + dv) = o4;
         }
     }
-    if (g_e == 0 && lse != nullptr) lse[rho] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
+    float* lse_dst = split ? part_lse + (int64_t)it.part * part_rows : lse;
+    if (g_e == 0 && lse_dst != nullptr)
+        lse_dst[rho] = ltot > 0.f ? (m_run + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -472,7 +458,7 @@ int prefill_absorbed_block_m() { return kBM; }
 hipError_t launch_prefill_absorbed(const LatentItem* items, int64_t n_items, const void* q,
                                    const void* kv, void* out, float* lse, int num_heads,
                                    float sm_scale, hipStream_t stream, const PagedKv* paged,
-                                   float* part_o, float* part_lse, int64_t part_rows) {
+                                   uint16_t* part_o, float* part_lse, int64_t part_rows) {
     if (n_items <= 0) return hipSuccess;
     if (n_items > 0x7fffffff) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
@@ -499,8 +485,8 @@ namespace {
 // One row per 128 lanes (two waves), 4 dims per lane. Each wave reads the
 // row's split LSEs in parallel (lane s takes split s) and reduces them with
 // cross-lane operations; the weights are then broadcast from their lanes,
-// and the partial rows are read a few splits at a time so that several
-// 16-byte loads are in flight.
+// and the partial rows (bf16) are read a few splits at a time so that
+// several loads are in flight.
 constexpr int kMergeThreads = 256;
 constexpr int kMaxSplits = 64;
 
@@ -516,7 +502,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
     int64_t rows, uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
     if (row >= rows) return;
@@ -529,21 +515,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
                         : __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);
     const float sum = wave_sum(w);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const float* src = part_o + row * kDv + c * 4;
+    const uint16_t* src = part_o + row * kDv + c * 4;
     const int64_t split_stride = rows * kDv;
     constexpr int kBatch = 4;
     for (int s0 = 0; s0 < splits; s0 += kBatch) {
-        f32x4_t v[kBatch];
+        bf16x4_t v[kBatch];
         float ws[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int sk = s0 + k < splits ? s0 + k : splits - 1;
             ws[k] = s0 + k < splits ? __shfl(w, sk) : 0.0f;
-            v[k] = ws[k] != 0.0f ? *reinterpret_cast<const f32x4_t*>(src + sk * split_stride)
-                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            v[k] = ws[k] != 0.0f ? *reinterpret_cast<const bf16x4_t*>(src + sk * split_stride)
+                                 : bf16x4_t{};
         }
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) acc += ws[k] * v[k];
+        for (int k = 0; k < kBatch; ++k) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += ws[k] * (float)v[k][e];
+        }
     }
     const float inv = sum > 0.f ? 1.0f / sum : 0.0f;
     bf16x4_t o4;
@@ -555,7 +544,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
 
 }  // namespace
 
-hipError_t launch_merge_splits(const float* part_o, const float* part_lse, int splits,
+hipError_t launch_merge_splits(const uint16_t* part_o, const float* part_lse, int splits,
                                int64_t rows, void* out, float* lse, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;

@@ -26,11 +26,11 @@ hipError_t launch_prefill_fp32(const WorkItem*, int64_t, const void*, const void
     return hipErrorInvalidValue;
 }
 hipError_t launch_prefill_absorbed(const LatentItem*, int64_t, const void*, const void*, void*,
-                                   float*, int, float, hipStream_t, const PagedKv*, float*, float*,
+                                   float*, int, float, hipStream_t, const PagedKv*, uint16_t*, float*,
                                    int64_t) {
     return hipErrorInvalidValue;
 }
-hipError_t launch_merge_splits(const float*, const float*, int, int64_t, void*, float*,
+hipError_t launch_merge_splits(const uint16_t*, const float*, int, int64_t, void*, float*,
                                hipStream_t) {
     return hipErrorInvalidValue;
 }
