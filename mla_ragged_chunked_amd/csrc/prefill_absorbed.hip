@@ -482,12 +482,13 @@ namespace {
 // keys, merged with the same log-sum-exp weights as merge_state):
 //   lse = ln sum_s e^lse_s,  o = sum_s e^(lse_s - lse) o_s;
 // splits with lse = -inf carry weight 0; all -inf gives o = 0, lse = -inf.
-// One row per 128 lanes (two waves), 4 dims per lane. Each wave reads the
-// row's split LSEs in parallel (lane s takes split s) and reduces them with
-// cross-lane operations; the weights are then broadcast from their lanes,
-// and the partial rows (bf16) are read a few splits at a time so that
-// several loads are in flight.
+// One row per wave, 8 dims (16 bytes of each bf16 partial) per lane. The
+// wave reads the row's split LSEs in parallel (lane s takes split s) and
+// reduces them with cross-lane operations; the weights are then broadcast
+// from their lanes, and the partial rows are read a few splits at a time so
+// that several loads are in flight.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeRows = kMergeThreads / 64;
 constexpr int kMaxSplits = 64;
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -504,9 +505,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
     int64_t rows, uint16_t* __restrict__ out, float* __restrict__ lse) {
-    const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+    // the row is the same for the whole wave, so a wave returns as a whole
+    const int64_t row = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const int c = threadIdx.x & 127;
     const int lane = threadIdx.x & 63;
     const float ls = lane < splits ? part_lse[(int64_t)lane * rows + row] : -INFINITY;
     const float mx = wave_max(ls);
@@ -514,32 +515,33 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
                         ? 0.0f
                         : __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);
     const float sum = wave_sum(w);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* src = part_o + row * kDv + c * 4;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const uint16_t* src = part_o + row * kDv + lane * 8;
     const int64_t split_stride = rows * kDv;
     constexpr int kBatch = 4;
     for (int s0 = 0; s0 < splits; s0 += kBatch) {
-        bf16x4_t v[kBatch];
+        bf16x8_t v[kBatch];
         float ws[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int sk = s0 + k < splits ? s0 + k : splits - 1;
             ws[k] = s0 + k < splits ? __shfl(w, sk) : 0.0f;
-            v[k] = ws[k] != 0.0f ? *reinterpret_cast<const bf16x4_t*>(src + sk * split_stride)
-                                 : bf16x4_t{};
+            v[k] = ws[k] != 0.0f
+                       ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(src + sk * split_stride))
+                       : bf16x8_t{};
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += ws[k] * (float)v[k][e];
+            for (int e = 0; e < 8; ++e) acc[e] += ws[k] * (float)v[k][e];
         }
     }
     const float inv = sum > 0.f ? 1.0f / sum : 0.0f;
-    bf16x4_t o4;
+    bf16x8_t o8;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x4_t*>(out + row * kDv + c * 4) = o4;
-    if (c == 0 && lse != nullptr) lse[row] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
+    for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x8_t*>(out + row * kDv + lane * 8) = o8;
+    if (lane == 0 && lse != nullptr) lse[row] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
 }
 
 }  // namespace
@@ -548,7 +550,7 @@ hipError_t launch_merge_splits(const uint16_t* part_o, const float* part_lse, in
                                int64_t rows, void* out, float* lse, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
-    const int64_t blocks = (rows + 1) / 2;
+    const int64_t blocks = (rows + kMergeRows - 1) / kMergeRows;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream,
                        part_o, part_lse, splits, rows, static_cast<uint16_t*>(out), lse);
